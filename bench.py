@@ -1,0 +1,268 @@
+"""Benchmark: denoise steps per second of one DiT denoising step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+A step is one call of dit_denoise_step: time embedding, context projection,
+patch embedding, every DiT block (LayerNorm+adaLN, QKV projection, RoPE,
+self-attention, gated output projection, cross-attention, GELU MLP) and the
+head, then the fused unpatchify + Euler update.  Inputs and weights are seeded
+synthetic data already resident in HBM when timing starts; the timestep and
+sigmas cycle through the workload's flow schedule.
+
+Prints ONE JSON line on stdout (diagnostics go to stderr):
+  value          whole-job steps/s (K timed steps, bracketed by
+                 torch.cuda.synchronize(), HIP events on the launch stream)
+  roofline       the kernel kind with the largest share of step time: its
+                 algorithmic FLOPs (or bytes) per launch over its average launch
+                 duration, from HIP events recorded around every launch during a
+                 second pass over the same K steps, against the MI355X peak
+  attention / gemm   TFLOP/s and fraction of the bf16 MFMA peak, same events
+  cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "denoise steps/sec per config + attention/GEMM TFLOP/s as % bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "image_s_bf16"
+
+GEMM_KINDS = ("gemm_qkv", "gemm_o", "gemm_cross_q", "gemm_cross_kv", "gemm_cross_o",
+              "gemm_mlp1_gelu", "gemm_mlp2", "gemm_text_proj", "gemm_patch_embed", "gemm_head")
+ATTN_KINDS = ("attention_self", "attention_cross")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kind_work(cfg) -> dict:
+    """Algorithmic work per launch of each kernel kind: ("flop", n) for matrix-core
+    kernels, ("byte", n) for bandwidth-bound ones (minimum HBM traffic)."""
+    S, D, F, L, P = cfg.tokens, cfg.hidden, cfg.mlp_hidden, cfg.ctx_len, cfg.patch_dim
+    es = 2 if cfg.dtype == "bf16" else 4
+    n_lat = cfg.latent_numel
+    return {
+        "gemm_qkv": ("flop", 2 * S * D * 3 * D),
+        "gemm_o": ("flop", 2 * S * D * D),
+        "gemm_cross_q": ("flop", 2 * S * D * D),
+        "gemm_cross_kv": ("flop", 2 * L * D * 2 * D),
+        "gemm_cross_o": ("flop", 2 * S * D * D),
+        "gemm_mlp1_gelu": ("flop", 2 * S * D * F),
+        "gemm_mlp2": ("flop", 2 * S * F * D),
+        "gemm_text_proj": ("flop", 2 * L * cfg.text_dim * D),
+        "gemm_patch_embed": ("flop", 2 * S * P * D),
+        "gemm_head": ("flop", 2 * S * D * P),
+        "attention_self": ("flop", 4 * S * S * D),
+        "attention_cross": ("flop", 4 * S * L * D),
+        # read the fp32 row, write the normalised row
+        "layernorm_modulate": ("byte", S * D * (4 + es)),
+        # read and write q and k, read the cos/sin tables
+        "rope": ("byte", 2 * 2 * S * D * es + S * cfg.head_dim * 4),
+        "patchify": ("byte", n_lat * (4 + es)),
+        # read velocity tokens, read-modify-write the latents
+        "unpatchify_euler": ("byte", n_lat * 4 * 3),
+        "time_embedding": ("byte", es * (cfg.freq_dim * D + D * D + 6 * D * D)),
+    }
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_kind: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel_kind}@{workload}")
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "diffusion_transformer_denoising_amd", "csrc", rec["source"])
+    if not os.path.exists(src) or source_hash(src) != rec["source_sha256_16"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(cfg, prm, X0, E, budget_s: float = 20.0) -> dict:
+    """The oracle as it stands, timed on the host cores over the first steps of
+    the same chain (as many as fit the budget, at least one)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    sig = oracle.flow_sigmas(cfg.steps, cfg.shift)
+    X = X0.astype(np.float64)
+    done = 0
+    t0 = time.perf_counter()
+    while done < cfg.steps:
+        t = float(np.float32(1000.0 * sig[done]))
+        X, _ = oracle.denoise_step(X, E, t, sig[done], sig[done + 1], prm, cfg)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {done} of the {cfg.steps} denoise steps of {cfg.name}, float64 numpy "
+                      f"oracle, {dt:.1f} s"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "the denoise step is sized for one GPU's share and nothing here uses a second.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from diffusion_transformer_denoising_amd import binding as B
+    from diffusion_transformer_denoising_amd.model import DeviceDiT, torch_dtype
+    from synth import params as SP
+    from synth.configs import get_config
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    cfg = get_config(args.workload)
+    log(f"[bench] workload {cfg.name}: S={cfg.tokens} D={cfg.hidden} B={cfg.num_blocks} "
+        f"H={cfg.heads}x{cfg.head_dim} F={cfg.mlp_hidden} L={cfg.ctx_len}")
+    t0 = time.perf_counter()
+    prm = SP.make_params(cfg)
+    X0 = SP.make_latents(cfg)
+    E = SP.make_ctx(cfg)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    m = DeviceDiT(cfg, prm)
+    X = torch.from_numpy(X0).cuda()
+    Ed = torch.from_numpy(E).cuda().to(torch_dtype(cfg))
+    sig = B.dit_flow_sigmas(cfg.steps, cfg.shift)
+    sched = [(float(np.float32(1000.0 * sig[k])), float(sig[k]), float(sig[k + 1]))
+             for k in range(cfg.steps)]
+
+    def run(n, k0=0):
+        for i in range(n):
+            t, s0, s1 = sched[(k0 + i) % cfg.steps]
+            m.denoise_step(X, Ed, t, s0, s1)
+
+    run(args.warmup)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    run(args.steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / args.steps
+    log(f"[bench] {args.steps} steps: {ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
+
+    # second pass over the same K steps with every launch bracketed by events
+    B.dit_profile_enable(m.handle, True)
+    run(args.steps)
+    torch.cuda.synchronize()
+    B.dit_profile_enable(m.handle, False)
+    prof = B.profile_summary(m.handle)
+    work = kind_work(cfg)
+    kernels = {}
+    for name, (n, tms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
+        unit, amount = work.get(name, ("flop", 0))
+        avg_s = tms / n / 1e3
+        rate = amount / avg_s if avg_s > 0 else 0.0
+        kernels[name] = {"launches": n, "avg_us": round(avg_s * 1e6, 3),
+                         "share": round(tms / sum(v[1] for v in prof.values()), 4),
+                         ("tflops" if unit == "flop" else "gbs"):
+                             round(rate / (1e12 if unit == "flop" else 1e9), 2)}
+        log(f"[bench]   {name:20s} {n:6d} x {avg_s * 1e6:9.2f} us  "
+            f"{rate / (1e12 if unit == 'flop' else 1e9):9.2f} {'TFLOP/s' if unit == 'flop' else 'GB/s'}")
+
+    def group_rate(kinds):
+        fl = sum(work[k][1] * prof[k][0] for k in kinds if k in prof)
+        tm = sum(prof[k][1] for k in kinds if k in prof) / 1e3
+        return (fl / tm / 1e12) if tm > 0 else 0.0
+
+    peak = PEAK_TFLOPS[cfg.dtype]
+    att_tf, gemm_tf = group_rate(ATTN_KINDS), group_rate(GEMM_KINDS)
+
+    dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    unit, amount = work[dom]
+    n_dom, ms_dom = prof[dom]
+    avg = ms_dom / n_dom / 1e3
+    src = "attention.hip" if dom.startswith("attention") else (
+        "gemm.hip" if dom.startswith("gemm") else "pointwise.hip")
+    if unit == "flop":
+        roof = {"bound": "mfma", "achieved": round(amount / avg / 1e12, 2), "peak": peak,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(amount / avg / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = measured_traffic(dom, cfg.name)
+    roof["kernel"] = dom
+    roof["per_launch"] = {"work": amount, "work_unit": "FLOP" if unit == "flop" else "byte",
+                          "avg_us": round(avg * 1e6, 3), "source": src}
+
+    fl = cfg.flops_per_step()
+    out = {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_step, 4),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded Philox N(0,1) latents/context, N(0,0.02^2) random-init weights)",
+        "config": {"workload": cfg.name, "tokens": cfg.tokens, "hidden": cfg.hidden,
+                   "blocks": cfg.num_blocks, "heads": cfg.heads, "head_dim": cfg.head_dim,
+                   "mlp_hidden": cfg.mlp_hidden, "ctx_len": cfg.ctx_len,
+                   "text_dim": cfg.text_dim, "latent": list(cfg.latent_shape),
+                   "schedule_steps": cfg.steps, "shift": cfg.shift, "batch": 1,
+                   "parallelism": "single GPU"},
+        "step_tflops": round(fl["total"] / (ms_per_step / 1e3) / 1e12, 2),
+        "step_frac_of_peak": round(fl["total"] / (ms_per_step / 1e3) / 1e12 / peak, 4),
+        "attention": {"tflops": round(att_tf, 2), "frac_of_peak": round(att_tf / peak, 4)},
+        "gemm": {"tflops": round(gemm_tf, 2), "frac_of_peak": round(gemm_tf / peak, 4)},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of the same workload")
+        out["cpu_baseline"] = cpu_baseline(cfg, prm, X0, E)
+    else:
+        out["cpu_baseline"] = None
+    m.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,516 @@
+// api.cpp -- the C ABI of libdit.so (declared in include/dit.h): argument
+// validation, the workspace plan, and the kernel sequence of one DiT block and
+// one denoise step on a single HIP stream.
+//
+// The sequence follows the denoiser as the SGLang-Diffusion pages frame it:
+// the DiT forward over patchified latents conditioned on the prompt
+// embeddings and the timestep ("Support New Diffusion Models", section
+// "2. Pipeline Config"), followed by the flow update driven by the sigma
+// schedule ("Disaggregated Diffusion Pipeline", section "Quick Start";
+// "Model Configuration Conventions", section "Sampling And Geometry").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <new>
+#include <vector>
+
+#include "dit.h"
+#include "kernels.h"
+
+using namespace dit;
+
+namespace {
+
+constexpr size_t WS_ALIGN = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace plan: every buffer the step needs, at 256-byte aligned offsets.
+struct Plan {
+  int64_t S, S_pad, L_pad, P, D, F, H, d;
+  size_t es;  // element size
+  size_t cos_t, sin_t, x, y, q, k, vt, o, h, c, kc, vct, patches, u, sinus, h1, temb, e, bmod,
+      hmod;
+  size_t total;
+};
+
+bool plan_layout(const dit_config &c, Plan &p) {
+  p.es = c.dtype == DIT_BF16 ? 2 : 4;
+  p.D = c.hidden;
+  p.F = c.mlp_hidden;
+  p.H = c.heads;
+  p.d = c.head_dim;
+  p.S = (int64_t)(c.lat_f / c.patch_f) * (c.lat_h / c.patch_h) * (c.lat_w / c.patch_w);
+  p.S_pad = (int64_t)round_up((size_t)p.S, 64);
+  p.L_pad = (int64_t)round_up((size_t)c.ctx_len_max, 64);
+  p.P = (int64_t)c.in_channels * c.patch_f * c.patch_h * c.patch_w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = round_up(off + bytes, WS_ALIGN);
+    return at;
+  };
+  const size_t f4 = 4, es = p.es;
+  p.cos_t = take(f4 * p.S * (p.d / 2));
+  p.sin_t = take(f4 * p.S * (p.d / 2));
+  p.x = take(f4 * p.S * p.D);
+  p.y = take(es * p.S * p.D);
+  p.q = take(es * p.S * p.D);
+  p.k = take(es * p.S * p.D);
+  p.vt = take(es * p.D * p.S_pad);
+  p.o = take(es * p.S * p.D);
+  p.h = take(es * p.S * p.F);
+  p.c = take(es * (size_t)c.ctx_len_max * p.D);
+  p.kc = take(es * (size_t)c.ctx_len_max * p.D);
+  p.vct = take(es * p.D * p.L_pad);
+  p.patches = take(es * p.S * p.P);
+  p.u = take(f4 * p.S * p.P);
+  p.sinus = take(f4 * c.freq_dim);
+  p.h1 = take(f4 * p.D);
+  p.temb = take(f4 * p.D);
+  p.e = take(f4 * 6 * p.D);
+  p.bmod = take(f4 * 6 * p.D * c.num_blocks);
+  p.hmod = take(f4 * 2 * p.D);
+  p.total = off;
+  return true;
+}
+
+dit_status check_config(const dit_config *c) {
+  if (!c) return DIT_ERR_INVALID_ARG;
+  if (c->dtype != DIT_F32 && c->dtype != DIT_BF16) return DIT_ERR_INVALID_ARG;
+  const int32_t pos[] = {c->num_blocks, c->hidden,  c->heads,   c->head_dim, c->mlp_hidden,
+                         c->freq_dim,   c->in_channels, c->patch_f, c->patch_h, c->patch_w,
+                         c->lat_f,      c->lat_h,   c->lat_w,   c->ctx_len_max, c->text_dim};
+  for (int32_t v : pos)
+    if (v <= 0) return DIT_ERR_SHAPE;
+  if (c->rope_f < 0 || c->rope_h < 0 || c->rope_w < 0) return DIT_ERR_SHAPE;
+  if (!(c->ln_eps > 0.0f) || !(c->rope_theta > 0.0f)) return DIT_ERR_INVALID_ARG;
+  if ((int64_t)c->heads * c->head_dim != c->hidden) return DIT_ERR_SHAPE;
+  if (c->lat_f % c->patch_f || c->lat_h % c->patch_h || c->lat_w % c->patch_w) return DIT_ERR_SHAPE;
+  if ((c->rope_f | c->rope_h | c->rope_w) & 1) return DIT_ERR_SHAPE;
+  if (c->rope_f + c->rope_h + c->rope_w != c->head_dim) return DIT_ERR_SHAPE;
+  if (c->freq_dim & 1) return DIT_ERR_SHAPE;
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128) return DIT_ERR_UNSUPPORTED;
+  // 16-byte vector moves along every contracted dimension and row.
+  const int64_t P = (int64_t)c->in_channels * c->patch_f * c->patch_h * c->patch_w;
+  if (c->hidden % 8 || c->mlp_hidden % 8 || c->text_dim % 8 || c->freq_dim % 8 || P % 8)
+    return DIT_ERR_UNSUPPORTED;
+  if (c->hidden > 5120 || c->hidden > 8192 || c->freq_dim > 8192) return DIT_ERR_UNSUPPORTED;
+  const int64_t S = (int64_t)(c->lat_f / c->patch_f) * (c->lat_h / c->patch_h) *
+                    (c->lat_w / c->patch_w);
+  if (S > (int64_t)1 << 30) return DIT_ERR_UNSUPPORTED;
+  return DIT_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool ok_ptr(const void *p) { return p != nullptr && aligned16(p); }
+
+dit_status hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_HIP; }
+
+#define DIT_TRY(expr)                        \
+  do {                                       \
+    hipError_t _e = (expr);                  \
+    if (_e != hipSuccess) return DIT_ERR_HIP; \
+  } while (0)
+
+// Launch `expr` on stream s; with profiling on, bracket it with two events.
+#define DIT_RUN(m, kind, s, expr)                                        \
+  do {                                                                   \
+    hipEvent_t _e0 = nullptr, _e1 = nullptr;                             \
+    if ((m)->prof.on) {                                                  \
+      _e0 = (m)->prof.get();                                             \
+      _e1 = (m)->prof.get();                                             \
+      if (!_e0 || !_e1) return DIT_ERR_HIP;                              \
+      DIT_TRY(hipEventRecord(_e0, s));                                   \
+    }                                                                    \
+    DIT_TRY(expr);                                                       \
+    if ((m)->prof.on) {                                                  \
+      DIT_TRY(hipEventRecord(_e1, s));                                   \
+      (m)->prof.recs.push_back({(int)(kind), (m)->prof.next - 2});       \
+    }                                                                    \
+  } while (0)
+
+// Kinds of timed launches (dit_profile_* report per kind).
+enum ProfKind {
+  PK_LN = 0, PK_GEMM_QKV, PK_ROPE, PK_ATTN_SELF, PK_GEMM_O, PK_GEMM_CQ, PK_GEMM_CKV,
+  PK_ATTN_CROSS, PK_GEMM_CO, PK_GEMM_MLP1, PK_GEMM_MLP2, PK_TIME, PK_GEMM_TXT, PK_PATCHIFY,
+  PK_GEMM_PE, PK_GEMM_OUT, PK_EULER, PK_COUNT
+};
+const char *const kProfNames[PK_COUNT] = {
+    "layernorm_modulate", "gemm_qkv", "rope", "attention_self", "gemm_o", "gemm_cross_q",
+    "gemm_cross_kv", "attention_cross", "gemm_cross_o", "gemm_mlp1_gelu", "gemm_mlp2",
+    "time_embedding", "gemm_text_proj", "patchify", "gemm_patch_embed", "gemm_head",
+    "unpatchify_euler"};
+
+// Optional per-launch timing: a start and an end event recorded on the launch
+// stream around each kernel.  Events are created on demand and reused.
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> events;
+  size_t next = 0;
+  std::vector<std::pair<int, size_t>> recs;  // (kind, index of the start event)
+  hipEvent_t get() {
+    if (next == events.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      events.push_back(e);
+    }
+    return events[next++];
+  }
+  ~Profiler() {
+    for (hipEvent_t e : events) (void)hipEventDestroy(e);
+  }
+};
+
+}  // namespace
+
+struct dit_model {
+  dit_config cfg;
+  DType dt;
+  dit_global_weights g;
+  std::vector<dit_block_weights> blocks;
+  char *ws;
+  Plan plan;
+  Profiler prof;
+  template <typename U> U *buf(size_t off) const { return reinterpret_cast<U *>(ws + off); }
+};
+
+namespace {
+
+dit_status check_global(const dit_config &c, const dit_global_weights &g) {
+  const void *req[] = {g.t1_w, g.t1_b, g.t2_w, g.t2_b, g.mod_w, g.mod_b,
+                       g.pe_w, g.pe_b, g.head_table, g.out_w, g.out_b};
+  for (const void *p : req)
+    if (!ok_ptr(p)) return DIT_ERR_INVALID_ARG;
+  if (c.text_dim != c.hidden && (!ok_ptr(g.txt_w) || !ok_ptr(g.txt_b))) return DIT_ERR_INVALID_ARG;
+  return DIT_OK;
+}
+
+dit_status check_block(const dit_block_weights &b) {
+  const void *req[] = {b.table, b.qkv_w, b.qkv_b, b.o_w, b.o_b, b.cq_w, b.cq_b, b.ckv_w,
+                       b.ckv_b, b.co_w,  b.co_b,  b.w1,  b.b1,  b.w2,   b.b2};
+  for (const void *p : req)
+    if (!ok_ptr(p)) return DIT_ERR_INVALID_ARG;
+  return DIT_OK;
+}
+
+GemmArgs gemm(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int N, int K,
+              const void *bias) {
+  GemmArgs a{};
+  a.A = A;
+  a.lda = lda;
+  a.W = W;
+  a.ldw = ldw;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.bias = bias;
+  return a;
+}
+
+// One block on the residual stream x [S, D] with projected context ctx [L, D].
+dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, const float *mod,
+                     hipStream_t s) {
+  const dit_config &c = m->cfg;
+  const Plan &p = m->plan;
+  const dit_block_weights &w = m->blocks[b];
+  const int S = (int)p.S, D = (int)p.D, F = (int)p.F;
+  void *y = m->buf<void>(p.y), *q = m->buf<void>(p.q), *k = m->buf<void>(p.k);
+  void *vt = m->buf<void>(p.vt), *o = m->buf<void>(p.o), *h = m->buf<void>(p.h);
+  void *kc = m->buf<void>(p.kc), *vct = m->buf<void>(p.vct);
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+
+  // self-attention branch: y = LN(x)(1 + scale_a) + shift_a
+  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, mod + 0 * D, mod + 1 * D, y, s));
+  {
+    GemmArgs a = gemm(y, D, w.qkv_w, D, S, 3 * D, D, w.qkv_b);
+    a.seg_width = D;
+    a.seg_ptr[0] = q; a.seg_ld[0] = D; a.seg_trans[0] = 0;
+    a.seg_ptr[1] = k; a.seg_ld[1] = D; a.seg_trans[1] = 0;
+    a.seg_ptr[2] = vt; a.seg_ld[2] = p.S_pad; a.seg_trans[2] = 1;
+    DIT_RUN(m, PK_GEMM_QKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
+  }
+  DIT_RUN(m, PK_ROPE, s, launch_rope(m->dt, q, k, D, S, c.heads, c.head_dim, m->buf<float>(p.cos_t),
+                      m->buf<float>(p.sin_t), s));
+  {
+    AttnArgs a{q, D, k, D, vt, p.S_pad, o, D, S, S, c.heads, c.head_dim, scale_log2};
+    DIT_RUN(m, PK_ATTN_SELF, s, launch_attention(m->dt, a, s));
+  }
+  {
+    GemmArgs a = gemm(o, D, w.o_w, D, S, D, D, w.o_b);
+    a.out = x; a.ldo = D; a.gate = mod + 2 * D;
+    DIT_RUN(m, PK_GEMM_O, s, launch_gemm(m->dt, EPI_RESIDUAL, a, s));
+  }
+  // cross-attention branch (plain LN, ungated)
+  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, nullptr, nullptr, y, s));
+  {
+    GemmArgs a = gemm(y, D, w.cq_w, D, S, D, D, w.cq_b);
+    a.out = q; a.ldo = D;
+    DIT_RUN(m, PK_GEMM_CQ, s, launch_gemm(m->dt, EPI_STORE, a, s));
+  }
+  {
+    GemmArgs a = gemm(ctx, D, w.ckv_w, D, L, 2 * D, D, w.ckv_b);
+    a.seg_width = D;
+    a.seg_ptr[0] = kc; a.seg_ld[0] = D; a.seg_trans[0] = 0;
+    a.seg_ptr[1] = vct; a.seg_ld[1] = p.L_pad; a.seg_trans[1] = 1;
+    DIT_RUN(m, PK_GEMM_CKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
+  }
+  {
+    AttnArgs a{q, D, kc, D, vct, p.L_pad, o, D, S, L, c.heads, c.head_dim, scale_log2};
+    DIT_RUN(m, PK_ATTN_CROSS, s, launch_attention(m->dt, a, s));
+  }
+  {
+    GemmArgs a = gemm(o, D, w.co_w, D, S, D, D, w.co_b);
+    a.out = x; a.ldo = D; a.gate = nullptr;
+    DIT_RUN(m, PK_GEMM_CO, s, launch_gemm(m->dt, EPI_RESIDUAL, a, s));
+  }
+  // MLP branch: y = LN(x)(1 + scale_f) + shift_f; x += gate_f * W2 gelu(W1 y + b1) + b2
+  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, mod + 3 * D, mod + 4 * D, y, s));
+  {
+    GemmArgs a = gemm(y, D, w.w1, D, S, F, D, w.b1);
+    a.out = h; a.ldo = F;
+    DIT_RUN(m, PK_GEMM_MLP1, s, launch_gemm(m->dt, EPI_GELU, a, s));
+  }
+  {
+    GemmArgs a = gemm(h, F, w.w2, F, S, D, F, w.b2);
+    a.out = x; a.ldo = D; a.gate = mod + 5 * D;
+    DIT_RUN(m, PK_GEMM_MLP2, s, launch_gemm(m->dt, EPI_RESIDUAL, a, s));
+  }
+  return DIT_OK;
+}
+
+dit_status run_time_path(dit_model *m, float t, float *bmod, float *hmod, float *temb,
+                         hipStream_t s) {
+  const dit_config &c = m->cfg;
+  const Plan &p = m->plan;
+  const int D = (int)p.D;
+  float *sinus = m->buf<float>(p.sinus), *h1 = m->buf<float>(p.h1), *e = m->buf<float>(p.e);
+  DIT_RUN(m, PK_TIME, s, launch_sinusoid(t, c.freq_dim, sinus, s));
+  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.t1_w, m->g.t1_b, sinus, h1, D, c.freq_dim, false, s));
+  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.t2_w, m->g.t2_b, h1, temb, D, D, true, s));
+  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.mod_w, m->g.mod_b, temb, e, 6 * D, D, true, s));
+  std::vector<const void *> tables(c.num_blocks);
+  for (int b = 0; b < c.num_blocks; ++b) tables[b] = m->blocks[b].table;
+  DIT_RUN(m, PK_TIME, s, launch_block_mods(m->dt, e, tables.data(), c.num_blocks, bmod, D, s));
+  DIT_RUN(m, PK_TIME, s, launch_head_mod(m->dt, m->g.head_table, temb, hmod, D, s));
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dit_status dit_workspace_size(const dit_config *cfg, size_t *bytes) {
+  if (!bytes) return DIT_ERR_INVALID_ARG;
+  *bytes = 0;
+  dit_status st = check_config(cfg);
+  if (st != DIT_OK) return st;
+  Plan p;
+  plan_layout(*cfg, p);
+  *bytes = p.total;
+  return DIT_OK;
+}
+
+dit_status dit_create(const dit_config *cfg, const dit_weights *weights, void *workspace,
+                      size_t workspace_bytes, void *stream, dit_model **out) {
+  if (!out) return DIT_ERR_INVALID_ARG;
+  *out = nullptr;
+  dit_status st = check_config(cfg);
+  if (st != DIT_OK) return st;
+  if (!weights || !weights->blocks) return DIT_ERR_INVALID_ARG;
+  if ((st = check_global(*cfg, weights->global)) != DIT_OK) return st;
+  for (int b = 0; b < cfg->num_blocks; ++b)
+    if ((st = check_block(weights->blocks[b])) != DIT_OK) return st;
+  if (!workspace || ((uintptr_t)workspace & (WS_ALIGN - 1))) return DIT_ERR_INVALID_ARG;
+  Plan p;
+  plan_layout(*cfg, p);
+  if (workspace_bytes < p.total) return DIT_ERR_WORKSPACE;
+
+  dit_model *m = new (std::nothrow) dit_model;
+  if (!m) return DIT_ERR_INVALID_ARG;
+  m->cfg = *cfg;
+  m->dt = cfg->dtype == DIT_BF16 ? DT_BF16 : DT_F32;
+  m->g = weights->global;
+  m->blocks.assign(weights->blocks, weights->blocks + cfg->num_blocks);
+  m->ws = static_cast<char *>(workspace);
+  m->plan = p;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_rope_tables(m->buf<float>(p.cos_t), m->buf<float>(p.sin_t),
+                                    cfg->lat_f / cfg->patch_f, cfg->lat_h / cfg->patch_h,
+                                    cfg->lat_w / cfg->patch_w, cfg->head_dim, cfg->rope_f,
+                                    cfg->rope_h, cfg->rope_w, cfg->rope_theta, s);
+  if (e != hipSuccess) {
+    delete m;
+    return DIT_ERR_HIP;
+  }
+  *out = m;
+  return DIT_OK;
+}
+
+dit_status dit_destroy(dit_model *model) {
+  delete model;
+  return DIT_OK;
+}
+
+dit_status dit_block_forward(dit_model *m, int32_t block, float *x, const void *ctx,
+                             int32_t ctx_len, const float *mod, void *stream) {
+  if (!m || !ok_ptr(x) || !ok_ptr(ctx) || !ok_ptr(mod)) return DIT_ERR_INVALID_ARG;
+  if (block < 0 || block >= m->cfg.num_blocks) return DIT_ERR_SHAPE;
+  if (ctx_len < 1 || ctx_len > m->cfg.ctx_len_max) return DIT_ERR_SHAPE;
+  return run_block(m, block, x, ctx, ctx_len, mod, static_cast<hipStream_t>(stream));
+}
+
+dit_status dit_denoise_step(dit_model *m, float *X, const void *ctx, int32_t ctx_len, float t,
+                            float sigma, float sigma_next, float *v_out, void *stream) {
+  if (!m || !ok_ptr(X) || !ok_ptr(ctx)) return DIT_ERR_INVALID_ARG;
+  if (v_out && !aligned16(v_out)) return DIT_ERR_INVALID_ARG;
+  if (!std::isfinite(t) || !std::isfinite(sigma) || !std::isfinite(sigma_next))
+    return DIT_ERR_INVALID_ARG;
+  if (ctx_len < 1 || ctx_len > m->cfg.ctx_len_max) return DIT_ERR_SHAPE;
+  const dit_config &c = m->cfg;
+  const Plan &p = m->plan;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int S = (int)p.S, D = (int)p.D, P = (int)p.P;
+  float *bmod = m->buf<float>(p.bmod), *hmod = m->buf<float>(p.hmod);
+  float *temb = m->buf<float>(p.temb), *x = m->buf<float>(p.x), *u = m->buf<float>(p.u);
+
+  dit_status st = run_time_path(m, t, bmod, hmod, temb, s);
+  if (st != DIT_OK) return st;
+
+  const void *cproj = ctx;
+  if (c.text_dim != c.hidden) {
+    GemmArgs a = gemm(ctx, c.text_dim, m->g.txt_w, c.text_dim, ctx_len, D, c.text_dim, m->g.txt_b);
+    a.out = m->buf<void>(p.c);
+    a.ldo = D;
+    DIT_RUN(m, PK_GEMM_TXT, s, launch_gemm(m->dt, EPI_STORE, a, s));
+    cproj = m->buf<void>(p.c);
+  }
+  DIT_RUN(m, PK_PATCHIFY, s, launch_patchify(m->dt, X, m->buf<void>(p.patches), c.in_channels, c.lat_f, c.lat_h,
+                          c.lat_w, c.patch_f, c.patch_h, c.patch_w, s));
+  {
+    GemmArgs a = gemm(m->buf<void>(p.patches), P, m->g.pe_w, P, S, D, P, m->g.pe_b);
+    a.out = x;
+    a.ldo = D;
+    DIT_RUN(m, PK_GEMM_PE, s, launch_gemm(m->dt, EPI_STORE_F32, a, s));
+  }
+  for (int b = 0; b < c.num_blocks; ++b) {
+    st = run_block(m, b, x, cproj, ctx_len, bmod + (int64_t)b * 6 * D, s);
+    if (st != DIT_OK) return st;
+  }
+  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, hmod, hmod + D, m->buf<void>(p.y), s));
+  {
+    GemmArgs a = gemm(m->buf<void>(p.y), D, m->g.out_w, D, S, P, D, m->g.out_b);
+    a.out = u;
+    a.ldo = P;
+    DIT_RUN(m, PK_GEMM_OUT, s, launch_gemm(m->dt, EPI_STORE_F32, a, s));
+  }
+  DIT_RUN(m, PK_EULER, s, launch_unpatchify_euler(u, X, v_out, sigma_next - sigma, c.in_channels, c.lat_f,
+                                  c.lat_h, c.lat_w, c.patch_f, c.patch_h, c.patch_w, s));
+  return DIT_OK;
+}
+
+dit_status dit_euler_step(float *X, const float *v, int64_t n, float sigma, float sigma_next,
+                          void *stream) {
+  if (n < 0) return DIT_ERR_SHAPE;
+  if (n == 0) return DIT_OK;
+  if (!ok_ptr(X) || !ok_ptr(v)) return DIT_ERR_INVALID_ARG;
+  if (!std::isfinite(sigma) || !std::isfinite(sigma_next)) return DIT_ERR_INVALID_ARG;
+  return hip_status(launch_euler(X, v, n, sigma_next - sigma, static_cast<hipStream_t>(stream)));
+}
+
+dit_status dit_flow_sigmas(int32_t n_steps, double shift, double *sigmas) {
+  if (!sigmas || !(shift > 0.0) || !std::isfinite(shift)) return DIT_ERR_INVALID_ARG;
+  if (n_steps < 1) return DIT_ERR_SHAPE;
+  for (int32_t k = 0; k <= n_steps; ++k) {
+    const double s = 1.0 - (double)k / (double)n_steps;
+    sigmas[k] = shift * s / (1.0 + (shift - 1.0) * s);
+  }
+  return DIT_OK;
+}
+
+dit_status dit_attention(int32_t dtype, int32_t heads, int32_t head_dim, const void *q,
+                         int64_t ldq, const void *k, int64_t ldk, const void *vt, int64_t ldv,
+                         void *o, int64_t ldo, int32_t sq, int32_t sk, void *stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_ERR_INVALID_ARG;
+  if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(vt) || !ok_ptr(o)) return DIT_ERR_INVALID_ARG;
+  if (heads < 1 || sq < 1 || sk < 1) return DIT_ERR_SHAPE;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return DIT_ERR_UNSUPPORTED;
+  const int64_t D = (int64_t)heads * head_dim;
+  if (ldq < D || ldk < D || ldo < D || ldv < (int64_t)round_up((size_t)sk, 64)) return DIT_ERR_SHAPE;
+  if ((ldq | ldk | ldv | ldo) & 7) return DIT_ERR_INVALID_ARG;
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  AttnArgs a{q, ldq, k, ldk, vt, ldv, o, ldo, sq, sk, heads, head_dim, scale_log2};
+  return hip_status(launch_attention(dtype == DIT_BF16 ? DT_BF16 : DT_F32, a,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+dit_status dit_layernorm_modulate(int32_t dtype, int32_t D, float eps, const float *x,
+                                  int32_t rows, const float *shift, const float *scale, void *y,
+                                  void *stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_ERR_INVALID_ARG;
+  if (!ok_ptr(x) || !ok_ptr(y)) return DIT_ERR_INVALID_ARG;
+  if ((shift == nullptr) != (scale == nullptr)) return DIT_ERR_INVALID_ARG;
+  if (shift && (!aligned16(shift) || !aligned16(scale))) return DIT_ERR_INVALID_ARG;
+  if (!(eps > 0.0f)) return DIT_ERR_INVALID_ARG;
+  if (rows < 0 || D < 4) return DIT_ERR_SHAPE;
+  if (D % 4 || D > 5120) return DIT_ERR_UNSUPPORTED;
+  return hip_status(launch_ln_modulate(dtype == DIT_BF16 ? DT_BF16 : DT_F32, x, rows, D, eps,
+                                       shift, scale, y, static_cast<hipStream_t>(stream)));
+}
+
+dit_status dit_time_embedding(dit_model *m, float t, float *block_mod, float *head_mod,
+                              float *temb, void *stream) {
+  if (!m || !ok_ptr(block_mod) || !ok_ptr(head_mod) || !ok_ptr(temb)) return DIT_ERR_INVALID_ARG;
+  if (!std::isfinite(t)) return DIT_ERR_INVALID_ARG;
+  return run_time_path(m, t, block_mod, head_mod, temb, static_cast<hipStream_t>(stream));
+}
+
+dit_status dit_profile_enable(dit_model *m, int32_t enable) {
+  if (!m) return DIT_ERR_INVALID_ARG;
+  m->prof.on = enable != 0;
+  if (m->prof.on) {
+    m->prof.next = 0;
+    m->prof.recs.clear();
+  }
+  return DIT_OK;
+}
+
+dit_status dit_profile_read(dit_model *m, int32_t kind, int64_t *launches, double *total_ms) {
+  if (!m || !launches || !total_ms) return DIT_ERR_INVALID_ARG;
+  if (kind < 0 || kind >= PK_COUNT) return DIT_ERR_SHAPE;
+  int64_t n = 0;
+  double ms = 0.0;
+  for (const auto &r : m->prof.recs) {
+    if (r.first != kind) continue;
+    hipEvent_t e0 = m->prof.events[r.second], e1 = m->prof.events[r.second + 1];
+    DIT_TRY(hipEventSynchronize(e1));
+    float t = 0.0f;
+    DIT_TRY(hipEventElapsedTime(&t, e0, e1));
+    ms += t;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = ms;
+  return DIT_OK;
+}
+
+int32_t dit_profile_kind_count(void) { return PK_COUNT; }
+
+const char *dit_profile_kind_name(int32_t kind) {
+  return (kind >= 0 && kind < PK_COUNT) ? kProfNames[kind] : nullptr;
+}
+
+const char *dit_status_string(dit_status s) {
+  switch (s) {
+    case DIT_OK: return "DIT_OK";
+    case DIT_ERR_INVALID_ARG: return "DIT_ERR_INVALID_ARG";
+    case DIT_ERR_SHAPE: return "DIT_ERR_SHAPE";
+    case DIT_ERR_UNSUPPORTED: return "DIT_ERR_UNSUPPORTED";
+    case DIT_ERR_WORKSPACE: return "DIT_ERR_WORKSPACE";
+    case DIT_ERR_HIP: return "DIT_ERR_HIP";
+  }
+  return "DIT_ERR_UNKNOWN";
+}
+
+}  // extern "C"

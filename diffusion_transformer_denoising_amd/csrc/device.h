@@ -1,0 +1,70 @@
+// device.h -- gfx950 device primitives shared by the DiT kernels: element
+// types, bf16 conversion, and the 32x32 MFMA fragment contract.
+//
+// MFMA fragment contract (v_mfma_f32_32x32x16_bf16 and, eight at a time,
+// v_mfma_f32_32x32x2_f32).  A "chunk" is 16 steps of the contracted index k.
+// For C[32x32] += A[32x16] * B[16x32]:
+//   A fragment: lane l holds row (l % 32), k = (l / 32) * 8 + e, e = 0..7;
+//   B fragment: lane l holds column (l % 32), k = (l / 32) * 8 + e;
+//   C:          lane l holds column (l % 32), rows j*8 + (l/32)*4 + i at
+//               acc[j*4 + i], i, j = 0..3.
+// With fp32 operands the chunk is eight 32x32x2 MFMAs; MFMA e takes element e
+// of every lane, i.e. k = e from lanes 0..31 and k = 8 + e from lanes 32..63,
+// so the fragment layout in registers is the same for both element types.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+__device__ __forceinline__ void mma32(const bf16x8 &a, const bf16x8 &b, f32x16 &c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(const f32x8 &a, const f32x8 &b, f32x16 &c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+}
+
+// 16-byte global/LDS vector moves.
+struct alignas(16) U128 { uint32_t w[4]; };
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// GELU, tanh form: z/2 (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3),
+// evaluated as z / (1 + exp(-2u)).
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  float u = k0 * (z + 0.044715f * z * z * z);
+  float e = fast_exp2(-2.0f * 1.4426950408889634f * u);
+  return z / (1.0f + e);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + fast_exp2(-1.4426950408889634f * z)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace dit

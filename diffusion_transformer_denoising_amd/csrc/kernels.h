@@ -1,0 +1,96 @@
+// kernels.h -- host-side launchers of the DiT kernels (internal to libdit.so).
+// Every launcher validates nothing: the C ABI layer checks shapes first.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+// GEMM  C[M, N] = A[M, K] * W[N, K]^T + bias[N], followed by one epilogue.
+enum Epilogue {
+  EPI_STORE = 0,     // out T [M, ldo]            = C
+  EPI_GELU = 1,      // out T [M, ldo]            = gelu_tanh(C)
+  EPI_RESIDUAL = 2,  // out float [M, ldo]       += gate[col] * C  (gate NULL: 1)
+  EPI_STORE_F32 = 3, // out float [M, ldo]        = C
+  EPI_SPLIT = 4,     // column segment s = col / seg_width goes to seg_ptr[s]:
+                     // row-major [M, seg_ld] or, when seg_trans[s], transposed
+                     // [seg_width, seg_ld] (element (row, c) at c * seg_ld + row)
+};
+
+struct GemmArgs {
+  const void *A;
+  int64_t lda;
+  const void *W;
+  int64_t ldw;
+  int M, N, K;
+  const void *bias;  // T [N] or NULL
+  void *out;
+  int64_t ldo;
+  const float *gate;  // EPI_RESIDUAL
+  int seg_width;      // EPI_SPLIT
+  void *seg_ptr[3];
+  int64_t seg_ld[3];
+  int seg_trans[3];
+};
+hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s);
+
+// Flash attention over heads: o = softmax(q k^T * scale) v, non-causal.
+// q [sq, ldq], k [sk, ldk], vt [heads*head_dim, ldv] (values transposed),
+// o [sq, ldo]; head h occupies columns h*head_dim .. of q, k and o.
+struct AttnArgs {
+  const void *q;
+  int64_t ldq;
+  const void *k;
+  int64_t ldk;
+  const void *vt;
+  int64_t ldv;
+  void *o;
+  int64_t ldo;
+  int sq, sk, heads, head_dim;
+  float scale_log2;  // log2(e) / sqrt(head_dim)
+};
+hipError_t launch_attention(DType dt, const AttnArgs &a, hipStream_t s);
+
+// y[r, :] = LN(x[r, :]) * (1 + scale) + shift  (plain LN when shift == scale == NULL)
+hipError_t launch_ln_modulate(DType dt, const float *x, int rows, int D, float eps,
+                              const float *shift, const float *scale, void *y, hipStream_t s);
+
+// In-place interleaved rotary rotation of q and k rows [S, ld] with tables
+// cos/sin [S, head_dim/2] (shared by all heads).
+hipError_t launch_rope(DType dt, void *q, void *k, int64_t ld, int S, int heads, int head_dim,
+                       const float *cos_t, const float *sin_t, hipStream_t s);
+
+// cos/sin [S, head_dim/2] for the patch grid (gf, gh, gw) and split (rf, rh, rw).
+hipError_t launch_rope_tables(float *cos_t, float *sin_t, int gf, int gh, int gw, int head_dim,
+                              int rf, int rh, int rw, float theta, hipStream_t s);
+
+// patches T [S, P] from latents X float [C, F, H, W].
+hipError_t launch_patchify(DType dt, const float *X, void *patches, int C, int F, int H, int W,
+                           int pf, int ph, int pw, hipStream_t s);
+
+// X += dt * unpatchify(u)  (u float [S, P]); v_out (nullable) = unpatchify(u).
+hipError_t launch_unpatchify_euler(const float *u, float *X, float *v_out, float dt, int C, int F,
+                                   int H, int W, int pf, int ph, int pw, hipStream_t s);
+
+// X[i] += dt * v[i], i < n.
+hipError_t launch_euler(float *X, const float *v, int64_t n, float dt, hipStream_t s);
+
+// Timestep sinusoid: out[j] = cos(t w_j), out[half + j] = sin(t w_j), w_j = 10000^(-j/half).
+hipError_t launch_sinusoid(float t, int dim, float *out, hipStream_t s);
+
+// y[n] = sum_k W[n, k] * act(x[k]) + b[n]; act = SiLU when silu_in, else identity.
+hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, float *y, int N,
+                       int K, bool silu_in, hipStream_t s);
+
+// block_mod[b, :, :] = e + table_b for up to `count` blocks starting at `first`;
+// tables T [6, D].
+hipError_t launch_block_mods(DType dt, const float *e, const void *const *tables, int count,
+                             float *block_mod, int D, hipStream_t s);
+
+// head_mod[j, :] = head_table[j, :] + temb, j = 0, 1.
+hipError_t launch_head_mod(DType dt, const void *head_table, const float *temb, float *head_mod,
+                           int D, hipStream_t s);
+
+}  // namespace dit

@@ -1,0 +1,378 @@
+// pointwise.hip -- the bandwidth-bound kernels of the denoise step:
+// LayerNorm + adaLN modulation, rotary embedding, patchify, fused
+// unpatchify + Euler update, and the small time-embedding path.
+#include "device.h"
+#include "kernels.h"
+
+namespace dit {
+
+// ---------------------------------------------------------------------------
+// LayerNorm + modulation.  One wave per row: the row is held in registers
+// (float4 per lane per 256 columns), mean and variance are two wave
+// reductions over the held values, then y = (x - mu) * rstd * (1 + scale) +
+// shift is written in the element type.  Rows up to 20 * 256 = 5120 wide.
+// ---------------------------------------------------------------------------
+constexpr int LN_MAXV = 20;
+
+template <typename T>
+__global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x, int rows, int D,
+                                                     float eps, const float *__restrict__ shift,
+                                                     const float *__restrict__ scale,
+                                                     T *__restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float *xr = x + (int64_t)row * D;
+  const int nv = D >> 2;  // float4 count
+  f32x4 v[LN_MAXV];
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int c = lane + i * 64;
+    if (c < nv) {
+      v[i] = *reinterpret_cast<const f32x4 *>(xr + 4 * c);
+      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+    }
+  }
+  const float mu = wave_sum(s) / (float)D;
+  float q = 0.0f;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int c = lane + i * 64;
+    if (c < nv) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d = v[i][e] - mu;
+        q += d * d;
+      }
+    }
+  }
+  const float var = wave_sum(q) / (float)D;
+  const float rstd = 1.0f / sqrtf(var + eps);
+  T *yr = y + (int64_t)row * D;
+#pragma unroll
+  for (int i = 0; i < LN_MAXV; ++i) {
+    const int c = lane + i * 64;
+    if (c < nv) {
+      f32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (v[i][e] - mu) * rstd;
+      if (shift) {
+        const f32x4 sh = *reinterpret_cast<const f32x4 *>(shift + 4 * c);
+        const f32x4 sc = *reinterpret_cast<const f32x4 *>(scale + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = o[e] * (1.0f + sc[e]) + sh[e];
+      }
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = (bf16)o[e];
+        *reinterpret_cast<bf16x4 *>(yr + 4 * c) = b;
+      } else {
+        *reinterpret_cast<f32x4 *>(yr + 4 * c) = o;
+      }
+    }
+  }
+}
+
+hipError_t launch_ln_modulate(DType dt, const float *x, int rows, int D, float eps,
+                              const float *shift, const float *scale, void *y, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (D % 4 != 0 || D > LN_MAXV * 256) return hipErrorInvalidValue;
+  dim3 grid((rows + 3) / 4);
+  if (dt == DT_BF16)
+    ln_mod_kernel<bf16><<<grid, 256, 0, s>>>(x, rows, D, eps, shift, scale, static_cast<bf16 *>(y));
+  else
+    ln_mod_kernel<float><<<grid, 256, 0, s>>>(x, rows, D, eps, shift, scale, static_cast<float *>(y));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Rotary embedding.  Pair (2j, 2j+1) of every head is rotated by the angle of
+// table column j of the token; one thread per (token, head, pair), q and k in
+// the same pass.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(T *__restrict__ q, T *__restrict__ k, int64_t ld,
+                                                   int S, int heads, int half_d,
+                                                   const float *__restrict__ cos_t,
+                                                   const float *__restrict__ sin_t) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)S * heads * half_d;
+  if (idx >= total) return;
+  const int j = (int)(idx % half_d);
+  const int64_t th = idx / half_d;
+  const int h = (int)(th % heads);
+  const int tok = (int)(th / heads);
+  const float c = cos_t[(int64_t)tok * half_d + j];
+  const float sn = sin_t[(int64_t)tok * half_d + j];
+  const int64_t off = (int64_t)tok * ld + (int64_t)h * 2 * half_d + 2 * j;
+  {
+    const float u0 = to_f32(q[off]), u1 = to_f32(q[off + 1]);
+    q[off] = from_f32<T>(u0 * c - u1 * sn);
+    q[off + 1] = from_f32<T>(u0 * sn + u1 * c);
+  }
+  {
+    const float u0 = to_f32(k[off]), u1 = to_f32(k[off + 1]);
+    k[off] = from_f32<T>(u0 * c - u1 * sn);
+    k[off + 1] = from_f32<T>(u0 * sn + u1 * c);
+  }
+}
+
+hipError_t launch_rope(DType dt, void *q, void *k, int64_t ld, int S, int heads, int head_dim,
+                       const float *cos_t, const float *sin_t, hipStream_t s) {
+  const int64_t total = (int64_t)S * heads * (head_dim / 2);
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (dt == DT_BF16)
+    rope_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<bf16 *>(q), static_cast<bf16 *>(k), ld, S,
+                                           heads, head_dim / 2, cos_t, sin_t);
+  else
+    rope_kernel<float><<<grid, 256, 0, s>>>(static_cast<float *>(q), static_cast<float *>(k), ld,
+                                            S, heads, head_dim / 2, cos_t, sin_t);
+  return hipGetLastError();
+}
+
+// Tables in double precision, rounded once: column j < rf/2 belongs to axis f
+// (pair j), then rh/2 columns of axis h, then rw/2 of axis w; the angle is
+// pos_axis * theta^(-2 j_axis / r_axis).
+__global__ void rope_table_kernel(float *cos_t, float *sin_t, int gf, int gh, int gw, int half_d,
+                                  int rf, int rh, int rw, double theta) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t S = (int64_t)gf * gh * gw;
+  if (idx >= S * half_d) return;
+  const int j = (int)(idx % half_d);
+  const int64_t tok = idx / half_d;
+  const int pw = (int)(tok % gw);
+  const int ph = (int)((tok / gw) % gh);
+  const int pf = (int)(tok / ((int64_t)gw * gh));
+  int pos, jj, width;
+  if (j < rf / 2) {
+    pos = pf; jj = j; width = rf;
+  } else if (j < (rf + rh) / 2) {
+    pos = ph; jj = j - rf / 2; width = rh;
+  } else {
+    pos = pw; jj = j - (rf + rh) / 2; width = rw;
+  }
+  const double phi = (double)pos * pow(theta, -2.0 * jj / (double)width);
+  cos_t[idx] = (float)cos(phi);
+  sin_t[idx] = (float)sin(phi);
+}
+
+hipError_t launch_rope_tables(float *cos_t, float *sin_t, int gf, int gh, int gw, int head_dim,
+                              int rf, int rh, int rw, float theta, hipStream_t s) {
+  const int64_t total = (int64_t)gf * gh * gw * (head_dim / 2);
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256));
+  rope_table_kernel<<<grid, 256, 0, s>>>(cos_t, sin_t, gf, gh, gw, head_dim / 2, rf, rh, rw,
+                                         (double)theta);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Patchify: token n = (f'*H' + h')*W' + w', element e = ((c*pf + i)*ph + j)*pw + k
+// holds X[c, f'*pf + i, h'*ph + j, w'*pw + k].  One thread per output element.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void patchify_kernel(const float *__restrict__ X,
+                                                       T *__restrict__ out, int C, int F, int H,
+                                                       int W, int pf, int ph, int pw) {
+  const int gh = H / ph, gw = W / pw;
+  const int P = C * pf * ph * pw;
+  const int64_t total = (int64_t)(F / pf) * gh * gw * P;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int e = (int)(idx % P);
+  const int64_t n = idx / P;
+  const int k = e % pw, j = (e / pw) % ph, i = (e / (pw * ph)) % pf, c = e / (pw * ph * pf);
+  const int w_ = (int)(n % gw), h_ = (int)((n / gw) % gh), f_ = (int)(n / ((int64_t)gw * gh));
+  const int64_t src = (((int64_t)c * F + f_ * pf + i) * H + h_ * ph + j) * W + w_ * pw + k;
+  out[idx] = from_f32<T>(X[src]);
+}
+
+hipError_t launch_patchify(DType dt, const float *X, void *patches, int C, int F, int H, int W,
+                           int pf, int ph, int pw, hipStream_t s) {
+  const int64_t total = (int64_t)C * F * H * W;
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (dt == DT_BF16)
+    patchify_kernel<bf16><<<grid, 256, 0, s>>>(X, static_cast<bf16 *>(patches), C, F, H, W, pf,
+                                               ph, pw);
+  else
+    patchify_kernel<float><<<grid, 256, 0, s>>>(X, static_cast<float *>(patches), C, F, H, W, pf,
+                                                ph, pw);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused unpatchify + Euler: one thread per latent element (c, f, h, w), which
+// reads its velocity from token/element of the patch layout, updates X in
+// place and optionally writes the velocity in latent layout.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void unpatchify_euler_kernel(const float *__restrict__ u,
+                                                               float *__restrict__ X,
+                                                               float *__restrict__ v_out,
+                                                               float dt, int C, int F, int H,
+                                                               int W, int pf, int ph, int pw) {
+  const int64_t total = (int64_t)C * F * H * W;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int w = (int)(idx % W);
+  const int h = (int)((idx / W) % H);
+  const int f = (int)((idx / ((int64_t)W * H)) % F);
+  const int c = (int)(idx / ((int64_t)W * H * F));
+  const int gh = H / ph, gw = W / pw;
+  const int P = C * pf * ph * pw;
+  const int64_t n = ((int64_t)(f / pf) * gh + h / ph) * gw + w / pw;
+  const int e = ((c * pf + f % pf) * ph + h % ph) * pw + w % pw;
+  const float v = u[n * P + e];
+  X[idx] = X[idx] + dt * v;
+  if (v_out) v_out[idx] = v;
+}
+
+hipError_t launch_unpatchify_euler(const float *u, float *X, float *v_out, float dt, int C, int F,
+                                   int H, int W, int pf, int ph, int pw, hipStream_t s) {
+  const int64_t total = (int64_t)C * F * H * W;
+  if (total <= 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256));
+  unpatchify_euler_kernel<<<grid, 256, 0, s>>>(u, X, v_out, dt, C, F, H, W, pf, ph, pw);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void euler_kernel(float *__restrict__ X,
+                                                    const float *__restrict__ v, int64_t n,
+                                                    float dt) {
+  const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i4 + 3 < n) {
+    f32x4 x = *reinterpret_cast<f32x4 *>(X + i4);
+    const f32x4 vv = *reinterpret_cast<const f32x4 *>(v + i4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = x[e] + dt * vv[e];
+    *reinterpret_cast<f32x4 *>(X + i4) = x;
+  } else {
+    for (int64_t i = i4; i < n; ++i) X[i] = X[i] + dt * v[i];
+  }
+}
+
+hipError_t launch_euler(float *X, const float *v, int64_t n, float dt, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t threads = (n + 3) / 4;
+  dim3 grid((unsigned)((threads + 255) / 256));
+  euler_kernel<<<grid, 256, 0, s>>>(X, v, n, dt);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Time path.
+// ---------------------------------------------------------------------------
+__global__ void sinusoid_kernel(double t, int half, float *out) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= half) return;
+  const double a = t * pow(10000.0, -(double)j / (double)half);
+  out[j] = (float)cos(a);
+  out[half + j] = (float)sin(a);
+}
+
+hipError_t launch_sinusoid(float t, int dim, float *out, hipStream_t s) {
+  const int half = dim / 2;
+  sinusoid_kernel<<<(half + 127) / 128, 128, 0, s>>>((double)t, half, out);
+  return hipGetLastError();
+}
+
+// One wave per output: the wave walks the weight row in 16-byte pieces.  The
+// input vector (SiLU applied when asked) is staged once per workgroup in LDS.
+constexpr int GEMV_MAXK = 8192;
+
+template <typename T>
+__global__ __launch_bounds__(256) void gemv_kernel(const T *__restrict__ W, const T *__restrict__ b,
+                                                   const float *__restrict__ x,
+                                                   float *__restrict__ y, int N, int K,
+                                                   int silu_in) {
+  constexpr int VEC = 16 / sizeof(T);
+  __shared__ float xs[GEMV_MAXK];
+  for (int k = threadIdx.x; k < K; k += 256) xs[k] = silu_in ? silu(x[k]) : x[k];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  const T *wr = W + (int64_t)n * K;
+  float acc = 0.0f;
+  for (int k0 = lane * VEC; k0 < K; k0 += 64 * VEC) {
+    U128 raw = *reinterpret_cast<const U128 *>(wr + k0);
+    const T *w = reinterpret_cast<const T *>(&raw);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc += to_f32(w[e]) * xs[k0 + e];
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) y[n] = acc + (b ? to_f32(b[n]) : 0.0f);
+}
+
+hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, float *y, int N,
+                       int K, bool silu_in, hipStream_t s) {
+  if (K > GEMV_MAXK) return hipErrorInvalidValue;
+  dim3 grid((N + 3) / 4);
+  if (dt == DT_BF16)
+    gemv_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<const bf16 *>(W),
+                                           static_cast<const bf16 *>(b), x, y, N, K, silu_in);
+  else
+    gemv_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(W),
+                                            static_cast<const float *>(b), x, y, N, K, silu_in);
+  return hipGetLastError();
+}
+
+constexpr int MOD_MAX_BLOCKS = 64;
+struct TablePtrs { const void *p[MOD_MAX_BLOCKS]; };
+
+template <typename T>
+__global__ __launch_bounds__(256) void block_mods_kernel(const float *__restrict__ e,
+                                                         TablePtrs tabs, int count,
+                                                         float *__restrict__ out, int D) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per = 6 * (int64_t)D;
+  if (idx >= per * count) return;
+  const int b = (int)(idx / per);
+  const int64_t r = idx - b * per;
+  out[idx] = e[r] + to_f32(static_cast<const T *>(tabs.p[b])[r]);
+}
+
+hipError_t launch_block_mods(DType dt, const float *e, const void *const *tables, int count,
+                             float *block_mod, int D, hipStream_t s) {
+  for (int first = 0; first < count; first += MOD_MAX_BLOCKS) {
+    const int n = count - first < MOD_MAX_BLOCKS ? count - first : MOD_MAX_BLOCKS;
+    TablePtrs tp;
+    for (int i = 0; i < n; ++i) tp.p[i] = tables[first + i];
+    const int64_t total = 6 * (int64_t)D * n;
+    dim3 grid((unsigned)((total + 255) / 256));
+    float *dst = block_mod + (int64_t)first * 6 * D;
+    if (dt == DT_BF16)
+      block_mods_kernel<bf16><<<grid, 256, 0, s>>>(e, tp, n, dst, D);
+    else
+      block_mods_kernel<float><<<grid, 256, 0, s>>>(e, tp, n, dst, D);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void head_mod_kernel(const T *__restrict__ table,
+                                                       const float *__restrict__ temb,
+                                                       float *__restrict__ out, int D) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= 2 * D) return;
+  out[i] = to_f32(table[i]) + temb[i % D];
+}
+
+hipError_t launch_head_mod(DType dt, const void *head_table, const float *temb, float *head_mod,
+                           int D, hipStream_t s) {
+  dim3 grid((2 * D + 255) / 256);
+  if (dt == DT_BF16)
+    head_mod_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<const bf16 *>(head_table), temb,
+                                               head_mod, D);
+  else
+    head_mod_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(head_table), temb,
+                                                head_mod, D);
+  return hipGetLastError();
+}
+
+}  // namespace dit

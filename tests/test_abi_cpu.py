@@ -1,0 +1,118 @@
+"""The C ABI on the CPU: the library loads, exports every function the header
+declares, and rejects bad arguments with the documented status codes before
+touching a device.  No call here launches GPU work."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from diffusion_transformer_denoising_amd import binding as B
+from synth.configs import CONFIGS
+
+
+def test_library_exports_every_header_function():
+    L = B.lib()
+    names = B.header_functions()
+    assert "dit_denoise_step" in names and "dit_euler_step" in names
+    assert "dit_create" in names and "dit_block_forward" in names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    assert B.status_string(B.DIT_OK) == "DIT_OK"
+    assert B.status_string(B.DIT_ERR_WORKSPACE) == "DIT_ERR_WORKSPACE"
+
+
+def test_flow_sigmas_host_matches_schedule():
+    for n, shift in [(4, 1.0), (50, 5.0), (20, 1.0), (1, 3.0)]:
+        got = np.array(B.dit_flow_sigmas(n, shift))
+        np.testing.assert_allclose(got, oracle.flow_sigmas(n, shift), rtol=0, atol=1e-15)
+    with pytest.raises(B.DitError) as e:
+        B.dit_flow_sigmas(0, 1.0)
+    assert e.value.status == B.DIT_ERR_SHAPE
+    with pytest.raises(B.DitError) as e:
+        B.dit_flow_sigmas(4, -1.0)
+    assert e.value.status == B.DIT_ERR_INVALID_ARG
+
+
+def test_workspace_size_valid_configs():
+    for cfg in CONFIGS.values():
+        assert B.dit_workspace_size(B.make_config(cfg)) > 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("hidden", 100, B.DIT_ERR_SHAPE),            # heads * head_dim != hidden
+    ("head_dim", 0, B.DIT_ERR_SHAPE),
+    ("rope_w", 15, B.DIT_ERR_SHAPE),             # odd / wrong sum
+    ("lat_h", 7, B.DIT_ERR_SHAPE),               # not divisible by the patch
+    ("ctx_len_max", 0, B.DIT_ERR_SHAPE),
+    ("dtype", 7, B.DIT_ERR_INVALID_ARG),
+    ("ln_eps", 0.0, B.DIT_ERR_INVALID_ARG),
+])
+def test_workspace_size_rejects(field, value, status):
+    c = B.make_config(CONFIGS["image_s_bf16"])
+    setattr(c, field, value)
+    with pytest.raises(B.DitError) as e:
+        B.dit_workspace_size(c)
+    assert e.value.status == status
+
+
+def test_unsupported_head_dim():
+    cfg = CONFIGS["image_s_bf16"].with_(heads=8, head_dim=96, rope=(0, 48, 48))
+    with pytest.raises(B.DitError) as e:
+        B.dit_workspace_size(B.make_config(cfg))
+    assert e.value.status == B.DIT_ERR_UNSUPPORTED
+
+
+def _fake_weights(cfg, ptr=4096):
+    gw = B.dit_global_weights()
+    for n in B.GLOBAL_FIELDS:
+        setattr(gw, n, ptr)
+    blocks = (B.dit_block_weights * cfg.num_blocks)()
+    for b in blocks:
+        for n in B.BLOCK_FIELDS:
+            setattr(b, n, ptr)
+    w = B.dit_weights()
+    w.global_ = gw
+    w.blocks = ctypes.cast(blocks, ctypes.POINTER(B.dit_block_weights))
+    return w, blocks
+
+
+def test_create_rejects_before_any_device_work():
+    cfg = CONFIGS["tiny_f32"]
+    c = B.make_config(cfg)
+    need = B.dit_workspace_size(c)
+    w, keep = _fake_weights(cfg)
+    # workspace too small
+    with pytest.raises(B.DitError) as e:
+        B.dit_create(c, w, 1 << 20, need - 1)
+    assert e.value.status == B.DIT_ERR_WORKSPACE
+    # null / misaligned workspace
+    with pytest.raises(B.DitError) as e:
+        B.dit_create(c, w, None, need)
+    assert e.value.status == B.DIT_ERR_INVALID_ARG
+    with pytest.raises(B.DitError) as e:
+        B.dit_create(c, w, (1 << 20) + 16, need)
+    assert e.value.status == B.DIT_ERR_INVALID_ARG
+    # a null or misaligned weight pointer
+    keep[0].w1 = None
+    with pytest.raises(B.DitError) as e:
+        B.dit_create(c, w, 1 << 20, need)
+    assert e.value.status == B.DIT_ERR_INVALID_ARG
+    keep[0].w1 = 4096 + 2
+    with pytest.raises(B.DitError) as e:
+        B.dit_create(c, w, 1 << 20, need)
+    assert e.value.status == B.DIT_ERR_INVALID_ARG
+
+
+def test_calls_reject_null_handle_and_bad_sizes():
+    L = B.lib()
+    assert L.dit_block_forward(None, 0, 4096, 4096, 1, 4096, None) == B.DIT_ERR_INVALID_ARG
+    assert L.dit_denoise_step(None, 4096, 4096, 1, 1.0, 1.0, 0.0, None, None) == B.DIT_ERR_INVALID_ARG
+    assert L.dit_euler_step(4096, 4096, -1, 1.0, 0.0, None) == B.DIT_ERR_SHAPE
+    assert L.dit_euler_step(None, None, 0, 1.0, 0.0, None) == B.DIT_OK      # empty: no-op
+    assert L.dit_euler_step(4098, 4096, 8, 1.0, 0.0, None) == B.DIT_ERR_INVALID_ARG
+    assert L.dit_euler_step(4096, 4096, 8, float("nan"), 0.0, None) == B.DIT_ERR_INVALID_ARG
+    assert L.dit_destroy(None) == B.DIT_OK
