@@ -74,6 +74,8 @@ _SIGS = {
     "dit_attention": ([c_i32, c_i32, c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64,
                        c_i32, c_i32, c_vp], c_i32),
     "dit_layernorm_modulate": ([c_i32, c_i32, c_f32, c_vp, c_i32, c_vp, c_vp, c_vp, c_vp], c_i32),
+    "dit_gemm": ([c_i32, c_i32, c_vp, c_i64, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_i64,
+                  c_vp, c_i32, c_vp], c_i32),
     "dit_time_embedding": ([c_vp, c_f32, c_vp, c_vp, c_vp, c_vp], c_i32),
     "dit_status_string": ([c_i32], ctypes.c_char_p),
     "dit_profile_enable": ([c_vp, c_i32], c_i32),
@@ -179,6 +181,16 @@ def dit_attention(dtype: int, heads: int, head_dim: int, q: int, ldq: int, k: in
                   vt: int, ldv: int, o: int, ldo: int, sq: int, sk: int, stream: int = 0) -> None:
     _check(lib().dit_attention(dtype, heads, head_dim, q, ldq, k, ldk, vt, ldv, o, ldo, sq, sk,
                                stream), "dit_attention")
+
+
+DIT_EPI_STORE, DIT_EPI_GELU, DIT_EPI_RESIDUAL, DIT_EPI_STORE_F32 = 0, 1, 2, 3
+
+
+def dit_gemm(dtype: int, epilogue: int, A: int, lda: int, W: int, ldw: int, M: int, N: int, K: int,
+             bias: int | None, out: int, ldo: int, gate: int | None = None, tile: int = 0,
+             stream: int = 0) -> None:
+    _check(lib().dit_gemm(dtype, epilogue, A, lda, W, ldw, M, N, K, bias, out, ldo, gate, tile,
+                          stream), "dit_gemm")
 
 
 def dit_layernorm_modulate(dtype: int, D: int, eps: float, x: int, rows: int, shift: int | None,

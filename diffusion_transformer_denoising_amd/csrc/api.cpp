@@ -445,6 +445,27 @@ dit_status dit_attention(int32_t dtype, int32_t heads, int32_t head_dim, const v
                                      static_cast<hipStream_t>(stream)));
 }
 
+dit_status dit_gemm(int32_t dtype, int32_t epilogue, const void *A, int64_t lda, const void *W,
+                    int64_t ldw, int32_t M, int32_t N, int32_t K, const void *bias, void *out,
+                    int64_t ldo, const float *gate, int32_t tile, void *stream) {
+  if (dtype != DIT_F32 && dtype != DIT_BF16) return DIT_ERR_INVALID_ARG;
+  if (epilogue < DIT_EPI_STORE || epilogue > DIT_EPI_STORE_F32) return DIT_ERR_INVALID_ARG;
+  if (!ok_ptr(A) || !ok_ptr(W) || !ok_ptr(out)) return DIT_ERR_INVALID_ARG;
+  if ((bias && !aligned16(bias)) || (gate && !aligned16(gate))) return DIT_ERR_INVALID_ARG;
+  if (tile < 0 || tile > 3) return DIT_ERR_INVALID_ARG;
+  if (M < 1 || N < 1 || K < 1 || lda < K || ldw < K || ldo < N) return DIT_ERR_SHAPE;
+  if ((K | lda | ldw | ldo) & 7) return DIT_ERR_UNSUPPORTED;
+  GemmArgs a = gemm(A, lda, W, ldw, M, N, K, bias);
+  a.out = out;
+  a.ldo = ldo;
+  a.gate = gate;
+  const Epilogue e = epilogue == DIT_EPI_STORE ? EPI_STORE
+                     : epilogue == DIT_EPI_GELU ? EPI_GELU
+                     : epilogue == DIT_EPI_RESIDUAL ? EPI_RESIDUAL : EPI_STORE_F32;
+  return hip_status(launch_gemm(dtype == DIT_BF16 ? DT_BF16 : DT_F32, e, a,
+                                static_cast<hipStream_t>(stream), tile));
+}
+
 dit_status dit_layernorm_modulate(int32_t dtype, int32_t D, float eps, const float *x,
                                   int32_t rows, const float *shift, const float *scale, void *y,
                                   void *stream) {

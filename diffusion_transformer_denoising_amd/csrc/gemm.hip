@@ -13,6 +13,8 @@
 // so the fragment reads of 16 consecutive rows hit distinct banks) and
 // prefetches the next slice into registers while the current one feeds the
 // MFMAs, so one barrier per K step suffices.
+#include <cmath>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -207,13 +209,31 @@ static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s) {
+// Tile choice: estimated time = (rounds of workgroups over the chip) x (tile
+// area / relative efficiency of that tile), with workgroups per CU set by LDS.
+static int pick_tile(int M, int N) {
+  struct C { int id, bm, bn, per_cu; double eff; };
+  const C cand[] = {{1, 256, 256, 1, 1.0}, {2, 128, 128, 2, 0.55}, {3, 64, 64, 4, 0.25}};
+  int best = 3;
+  double best_t = 1e300;
+  for (const C &c : cand) {
+    const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    const double rounds = std::ceil(tiles / (256.0 * c.per_cu));
+    const double t = rounds * c.per_cu * (double)c.bm * c.bn / c.eff;
+    if (t < best_t) { best_t = t; best = c.id; }
+  }
+  return best;
+}
+
+hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipSuccess;
   if (dt == DT_BF16) {
-    // Small problems use 64x64 tiles so that the grid still covers the chip.
-    const int64_t tiles128 = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-    if (tiles128 >= 512) return launch_t<bf16, 128, 128>(epi, a, s);
-    return launch_t<bf16, 64, 64>(epi, a, s);
+    if (tile == 0) tile = pick_tile(a.M, a.N);
+    switch (tile) {
+      case 1: return launch_t<bf16, 256, 256>(epi, a, s);
+      case 2: return launch_t<bf16, 128, 128>(epi, a, s);
+      default: return launch_t<bf16, 64, 64>(epi, a, s);
+    }
   }
   return launch_t<float, 64, 64>(epi, a, s);
 }

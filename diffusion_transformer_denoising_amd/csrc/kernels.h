@@ -34,7 +34,8 @@ struct GemmArgs {
   int64_t seg_ld[3];
   int seg_trans[3];
 };
-hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s);
+// tile: 0 automatic, 1 256x256, 2 128x128, 3 64x64 (bf16); fp32 uses 64x64.
+hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile = 0);
 
 // Flash attention over heads: o = softmax(q k^T * scale) v, non-causal.
 // q [sq, ldq], k [sk, ldk], vt [heads*head_dim, ldv] (values transposed),

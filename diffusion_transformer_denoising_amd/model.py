@@ -56,6 +56,14 @@ def layernorm_modulate(dtype: str, eps: float, x, shift, scale, y, stream=None):
                              y.data_ptr(), _stream_of(x.device, stream))
 
 
+def gemm(dtype: str, epilogue: int, A, W, bias, out, gate=None, tile: int = 0, stream=None):
+    """dit_gemm on torch tensors: out (+)= epilogue(A @ W^T + bias)."""
+    B.dit_gemm(B.DIT_BF16 if dtype == "bf16" else B.DIT_F32, epilogue, A.data_ptr(), A.stride(0),
+               W.data_ptr(), W.stride(0), A.shape[0], W.shape[0], A.shape[1],
+               bias.data_ptr() if bias is not None else None, out.data_ptr(), out.stride(0),
+               gate.data_ptr() if gate is not None else None, tile, _stream_of(A.device, stream))
+
+
 class DeviceDiT:
     def __init__(self, cfg, params: dict, device: str = "cuda", stream: int | None = None):
         self.cfg = cfg

@@ -190,6 +190,21 @@ dit_status dit_attention(int32_t dtype, int32_t heads, int32_t head_dim, const v
                          int64_t ldq, const void *k, int64_t ldk, const void *vt, int64_t ldv,
                          void *o, int64_t ldo, int32_t sq, int32_t sk, void *stream);
 
+/* Linear layer on the matrix cores, C[M, N] = A[M, K] * W[N, K]^T + bias[N]
+ * (the step's projection kernel), followed by one epilogue:
+ *   DIT_EPI_STORE     out T [M, ldo]       = C
+ *   DIT_EPI_GELU      out T [M, ldo]       = GELU_tanh(C)
+ *   DIT_EPI_RESIDUAL  out float [M, ldo]  += gate[n] * C   (gate NULL: 1)
+ *   DIT_EPI_STORE_F32 out float [M, ldo]   = C
+ * A device T [M, lda], W device T [N, ldw], bias device T [N] or NULL.
+ * M, N, K >= 1; K and every leading dimension a multiple of 8; lda, ldw >= K;
+ * ldo >= N.  tile selects the workgroup tile (0 automatic, 1: 256x256,
+ * 2: 128x128, 3: 64x64; fp32 always uses 64x64). */
+enum { DIT_EPI_STORE = 0, DIT_EPI_GELU = 1, DIT_EPI_RESIDUAL = 2, DIT_EPI_STORE_F32 = 3 };
+dit_status dit_gemm(int32_t dtype, int32_t epilogue, const void *A, int64_t lda, const void *W,
+                    int64_t ldw, int32_t M, int32_t N, int32_t K, const void *bias, void *out,
+                    int64_t ldo, const float *gate, int32_t tile, void *stream);
+
 /* LayerNorm without affine parameters over rows of x (device float [rows, D]),
  * y = LN(x) * (1 + scale) + shift when shift and scale (device float [D]) are
  * both given, plain LN(x) when both are NULL; y is device T [rows, D].

@@ -1,0 +1,87 @@
+"""Kernel-level parity through the C ABI component entry points: the GEMM in
+every tile configuration and epilogue (ragged M, N and K), against the
+oracle's float64 Linear and elementwise definitions."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from diffusion_transformer_denoising_amd import binding as B
+from diffusion_transformer_denoising_amd.model import gemm
+from tests.gpu_helpers import announce, dev_tensor, rel_l2, require_gpu, storage_round, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _gemm_case(dtype, epi, M, N, K, tile, seed=0):
+    rng = np.random.default_rng(seed)
+    A = storage_round(rng.standard_normal((M, K)), dtype)
+    W = storage_round(rng.standard_normal((N, K)) * 0.05, dtype)
+    b = storage_round(rng.standard_normal(N) * 0.1, dtype)
+    gate = rng.standard_normal(N).astype(np.float32)
+    x0 = rng.standard_normal((M, N)).astype(np.float32)
+    Ad, Wd, bd = dev_tensor(A, dtype), dev_tensor(W, dtype), dev_tensor(b, dtype)
+    if epi in (B.DIT_EPI_STORE, B.DIT_EPI_GELU):
+        out = torch.zeros((M, N), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
+                          device="cuda")
+    elif epi == B.DIT_EPI_RESIDUAL:
+        out = torch.from_numpy(x0).cuda()
+    else:
+        out = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    gd = torch.from_numpy(gate).cuda() if epi == B.DIT_EPI_RESIDUAL else None
+    gemm(dtype, epi, Ad, Wd, bd, out, gate=gd, tile=tile)
+    torch.cuda.synchronize()
+    C = oracle.linear(A, W, b)
+    if epi == B.DIT_EPI_GELU:
+        ref = oracle.gelu_tanh(C)
+    elif epi == B.DIT_EPI_RESIDUAL:
+        ref = x0 + gate * C
+    else:
+        ref = C
+    got = to_np(out)
+    if epi == B.DIT_EPI_RESIDUAL:
+        return rel_l2(got - x0, ref - x0)
+    return rel_l2(got, ref)
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
+                                 B.DIT_EPI_STORE_F32])
+@pytest.mark.parametrize("M,N,K", [(1000, 700, 520), (300, 260, 64), (513, 1024, 1536)])
+def test_gemm_bf16_tiles(tile, epi, M, N, K):
+    require_gpu()
+    announce("gemm bf16", tile, epi, M, N, K)
+    err = _gemm_case("bf16", epi, M, N, K, tile)
+    # bf16 output rounding (2^-9 relative) dominates for the T outputs
+    tol = 5e-3 if epi in (B.DIT_EPI_STORE, B.DIT_EPI_GELU) else 1e-5
+    assert err < tol, err
+
+
+@pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
+                                 B.DIT_EPI_STORE_F32])
+@pytest.mark.parametrize("M,N,K", [(16, 64, 16), (100, 72, 264), (77, 16, 64)])
+def test_gemm_f32(epi, M, N, K):
+    require_gpu()
+    announce("gemm f32", epi, M, N, K)
+    assert _gemm_case("f32", epi, M, N, K, 0) < 1e-5
+
+
+def test_gemm_full_size_sampled_rows():
+    """MLP-1 of the Wan-14B shape (32760 x 13824 x 5120) in the launch
+    configuration the step uses; 64 sampled output rows against float64."""
+    require_gpu()
+    announce("gemm full-size wan14b mlp1")
+    rng = np.random.default_rng(3)
+    M, N, K = 32760, 13824, 5120
+    A = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+    W = (torch.randn((N, K), device="cuda") * 0.02).to(torch.bfloat16)
+    b = (torch.randn(N, device="cuda") * 0.02).to(torch.bfloat16)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gemm("bf16", B.DIT_EPI_GELU, A, W, b, out)
+    torch.cuda.synchronize()
+    rows = np.sort(rng.choice(M, 64, replace=False))
+    rows[-1] = M - 1                                   # the ragged last tile
+    Ah = to_np(A[torch.from_numpy(rows).cuda()])
+    ref = oracle.gelu_tanh(oracle.linear(Ah, to_np(W), to_np(b)))
+    got = to_np(out[torch.from_numpy(rows).cuda()])
+    assert rel_l2(got, ref) < 5e-3
