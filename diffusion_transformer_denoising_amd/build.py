@@ -25,7 +25,7 @@ ARCH = "gfx950"
 SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "pointwise.hip"]
 
 HIP_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     "-I", INCLUDE, "-I", CSRC,
     # no packed-fp32 VALU instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -100,6 +100,10 @@ dit_status check_config(const dit_config *c) {
   const int64_t S = (int64_t)(c->lat_f / c->patch_f) * (c->lat_h / c->patch_h) *
                     (c->lat_w / c->patch_w);
   if (S > (int64_t)1 << 30) return DIT_ERR_UNSUPPORTED;
+  const DType dt = c->dtype == DIT_BF16 ? DT_BF16 : DT_F32;
+  if (!gemm_offsets_fit(dt, S, c->mlp_hidden, 3 * (int64_t)c->hidden, c->mlp_hidden) ||
+      !gemm_offsets_fit(dt, c->ctx_len_max, c->text_dim, c->mlp_hidden, c->hidden))
+    return DIT_ERR_UNSUPPORTED;
   return DIT_OK;
 }
 
@@ -454,7 +458,9 @@ dit_status dit_gemm(int32_t dtype, int32_t epilogue, const void *A, int64_t lda,
   if ((bias && !aligned16(bias)) || (gate && !aligned16(gate))) return DIT_ERR_INVALID_ARG;
   if (tile < 0 || tile > 3) return DIT_ERR_INVALID_ARG;
   if (M < 1 || N < 1 || K < 1 || lda < K || ldw < K || ldo < N) return DIT_ERR_SHAPE;
-  if ((K | lda | ldw | ldo) & 7) return DIT_ERR_UNSUPPORTED;
+  if ((K | lda | ldw) & 7) return DIT_ERR_UNSUPPORTED;
+  if (!gemm_offsets_fit(dtype == DIT_BF16 ? DT_BF16 : DT_F32, M, lda, N, ldw))
+    return DIT_ERR_UNSUPPORTED;
   GemmArgs a = gemm(A, lda, W, ldw, M, N, K, bias);
   a.out = out;
   a.ldo = ldo;

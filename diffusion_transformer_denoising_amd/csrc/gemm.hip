@@ -35,6 +35,18 @@ __device__ __forceinline__ typename Frag<T>::type lds_frag(const T *p) {
   }
 }
 
+// Raw buffer resource over `bytes` bytes: loads at offsets past the end
+// return zero, which handles ragged M, N and K without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(U128, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every operand (sizes < 2^31 bytes)
+
 template <typename T, int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   constexpr int BK = 128 / sizeof(T);   // elements in a 128-byte row slice
@@ -43,8 +55,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   constexpr int CHUNKS = BK / 16;       // MFMA k-chunks per slice
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int LA = BM * 8 / 256;      // 16-byte loads per thread for A
-  constexpr int LW = BN * 8 / 256;
+  constexpr int LA = BM / 32;           // 16-byte loads per thread per slice (A)
+  constexpr int LW = BN / 32;           // (W)
   typedef typename Frag<T>::type F;
 
   __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * ROW];
@@ -55,44 +67,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM;
   const int n0 = blockIdx.x * BN;
-  const T *A = static_cast<const T *>(p.A);
-  const T *W = static_cast<const T *>(p.W);
   const int M = p.M, N = p.N, K = p.K;
 
-  U128 ra[LA], rw[LW];
-  auto gload = [&](int kt) {
+  // Each thread moves the 16-byte piece kk of rows (tid >> 3) + 32 i.
+  const int kk = (tid & 7) * VEC;
+  const int r0 = tid >> 3;
+  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(p.A, (uint32_t)((int64_t)M * p.lda * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rw_src = make_rsrc(p.W, (uint32_t)((int64_t)N * p.ldw * sizeof(T)));
+  const uint32_t a_off0 = (uint32_t)(((int64_t)(m0 + r0) * p.lda + kk) * sizeof(T));
+  const uint32_t w_off0 = (uint32_t)(((int64_t)(n0 + r0) * p.ldw + kk) * sizeof(T));
+  const uint32_t a_step = (uint32_t)(32 * p.lda * sizeof(T));
+  const uint32_t w_step = (uint32_t)(32 * p.ldw * sizeof(T));
+
+  // Staging registers for one slice: pieces 0..LA-1 are A rows, LA.. are W rows.
+  constexpr int NP = LA + LW;
+  U128 stage[NP];
+  auto gload_piece = [&](int i, int kt) {
     const int k0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int c = tid + i * 256, r = c >> 3, kk = (c & 7) * VEC;
-      const int gm = m0 + r, gk = k0 + kk;
-      if (gm < M && gk < K)
-        ra[i] = *reinterpret_cast<const U128 *>(A + (int64_t)gm * p.lda + gk);
-      else
-        ra[i] = U128{{0u, 0u, 0u, 0u}};
-    }
-#pragma unroll
-    for (int i = 0; i < LW; ++i) {
-      const int c = tid + i * 256, r = c >> 3, kk = (c & 7) * VEC;
-      const int gn = n0 + r, gk = k0 + kk;
-      if (gn < N && gk < K)
-        rw[i] = *reinterpret_cast<const U128 *>(W + (int64_t)gn * p.ldw + gk);
-      else
-        rw[i] = U128{{0u, 0u, 0u, 0u}};
-    }
+    const bool kin = (k0 + kk) < K;
+    const uint32_t kb = (uint32_t)(k0 * sizeof(T));
+    if (i < LA)
+      stage[i] = buf_load16(ra_src, kin ? a_off0 + i * a_step + kb : OOB);
+    else
+      stage[i] = buf_load16(rw_src, kin ? w_off0 + (i - LA) * w_step + kb : OOB);
   };
-  auto sstore = [&](int buf) {
-    T *base = lds[buf];
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int c = tid + i * 256, r = c >> 3, kk = (c & 7) * VEC;
-      *reinterpret_cast<U128 *>(base + r * ROW + kk) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < LW; ++i) {
-      const int c = tid + i * 256, r = c >> 3, kk = (c & 7) * VEC;
-      *reinterpret_cast<U128 *>(base + (BM + r) * ROW + kk) = rw[i];
-    }
+  auto sstore_piece = [&](int i, T *base) {
+    const int row = i < LA ? r0 + 32 * i : BM + r0 + 32 * (i - LA);
+    *reinterpret_cast<U128 *>(base + row * ROW + kk) = stage[i];
   };
 
   f32x16 acc[TM][TN];
@@ -103,31 +104,90 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
 
+  // fragment source rows of this lane within the LDS tile
+  const int arow = (wm * WM + (lane & 31)) * ROW + (lane >> 5) * 8;
+  const int wrow = (BM + wn * WN + (lane & 31)) * ROW + (lane >> 5) * 8;
+  F af[2][TM], wf[2][TN];
+  auto lload = [&](const T *base, int ch, int slot) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a) af[slot][a] = lds_frag<T>(base + arow + a * 32 * ROW + ch * 16);
+#pragma unroll
+    for (int b = 0; b < TN; ++b) wf[slot][b] = lds_frag<T>(base + wrow + b * 32 * ROW + ch * 16);
+  };
+
+  // Schedule of one K step (slice kt in LDS buffer cur, slice kt+1 in the
+  // staging registers):
+  //   chunks 0 .. CHUNKS-2: read the next chunk's fragments, issue this
+  //     chunk's MFMAs, and move a share of slice kt+1 from the staging
+  //     registers into the other LDS buffer, refilling each register with
+  //     slice kt+2 right after it is stored;
+  //   barrier (all fragments of slice kt are in registers, slice kt+1 is in
+  //     LDS), then the last chunk's MFMAs overlap with reading the first
+  //     fragments of slice kt+1.
+  // The buffer written during step kt was last read before the previous
+  // step's barrier, so one barrier per step suffices.
+  constexpr int PER = (NP + CHUNKS - 2) / (CHUNKS - 1);
   const int KT = (K + BK - 1) / BK;
-  gload(0);
-  sstore(0);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) gload_piece(i, 0);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) sstore_piece(i, lds[0]);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) gload_piece(i, 1);
   __syncthreads();
+  lload(lds[0], 0, 0);
+  // Instruction mix per chunk, for pinning the schedule: MFMAs, fragment
+  // reads, and (chunks 0 .. CHUNKS-2) staging stores + global loads.
+  constexpr int NM = TM * TN * (sizeof(T) == 2 ? 1 : 8);
+  constexpr int NR = (TM + TN) * (sizeof(T) == 2 ? 1 : 2);
+  constexpr bool PIN = NM >= NR;
+
+  // The step body is branch-free: past the last slice the loads fall out of
+  // range and return zero, and the stores go to a buffer nobody reads again.
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
     const T *base = lds[cur];
-#pragma unroll
-    for (int ch = 0; ch < CHUNKS; ++ch) {
-      const int kk = ch * 16 + (lane >> 5) * 8;
-      F af[TM], wf[TN];
+    T *next = lds[cur ^ 1];
+    static_for<CHUNKS>([&](auto CH) {
+      constexpr int ch = CH;
+      constexpr int slot = ch & 1;
+      if constexpr (ch + 1 < CHUNKS) {
+        lload(base, ch + 1, slot ^ 1);
+      } else {
+        __syncthreads();
+        lload(next, 0, slot ^ 1);
+      }
 #pragma unroll
       for (int a = 0; a < TM; ++a)
-        af[a] = lds_frag<T>(base + (wm * WM + a * 32 + (lane & 31)) * ROW + kk);
 #pragma unroll
-      for (int b = 0; b < TN; ++b)
-        wf[b] = lds_frag<T>(base + (BM + wn * WN + b * 32 + (lane & 31)) * ROW + kk);
+        for (int b = 0; b < TN; ++b) mma32(af[slot][a], wf[slot][b], acc[a][b]);
+      // staging pieces moved during this chunk
+      constexpr int first = ch * PER;
+      constexpr int nw = ch + 1 < CHUNKS ? (NP - first < PER ? (NP - first > 0 ? NP - first : 0) : PER) : 0;
 #pragma unroll
-      for (int a = 0; a < TM; ++a)
-#pragma unroll
-        for (int b = 0; b < TN; ++b) mma32(af[a], wf[b], acc[a][b]);
-    }
-    if (kt + 1 < KT) sstore(cur ^ 1);
-    __syncthreads();
+      for (int i = first; i < first + nw; ++i) {
+        sstore_piece(i, next);
+        gload_piece(i, kt + 2);
+      }
+      if constexpr (PIN) {
+        // fragment reads paired with MFMAs, then store + load (+ MFMA while
+        // any are left), then the remaining MFMAs
+        constexpr int PAIRS = NR < NM ? NR : NM;
+        static_for<PAIRS>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        });
+        constexpr int WM_ = nw < NM - PAIRS ? nw : NM - PAIRS;  // stores that get an MFMA
+        static_for<nw>([&](auto W) {
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+          if constexpr (W < WM_) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        });
+        constexpr int left = NM - PAIRS - WM_;
+        if constexpr (left > 0) __builtin_amdgcn_sched_group_barrier(0x008, left, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
   }
 
   // ---- epilogue: lane holds column (lane & 31), rows j*8 + (lane>>5)*4 + i
@@ -209,6 +269,12 @@ static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) {
+  // 32-bit byte offsets, including the rows of the last (partial) tile
+  const int64_t es = dt == DT_BF16 ? 2 : 4, lim = (int64_t)1 << 31;
+  return (M + 256) * lda * es < lim && (N + 256) * ldw * es < lim;
+}
+
 // Tile choice: estimated time = (rounds of workgroups over the chip) x (tile
 // area / relative efficiency of that tile), with workgroups per CU set by LDS.
 static int pick_tile(int M, int N) {
@@ -227,6 +293,7 @@ static int pick_tile(int M, int N) {
 
 hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipSuccess;
+  if (!gemm_offsets_fit(dt, a.M, a.lda, a.N, a.ldw)) return hipErrorInvalidValue;
   if (dt == DT_BF16) {
     if (tile == 0) tile = pick_tile(a.M, a.N);
     switch (tile) {

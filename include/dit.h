@@ -197,7 +197,7 @@ dit_status dit_attention(int32_t dtype, int32_t heads, int32_t head_dim, const v
  *   DIT_EPI_RESIDUAL  out float [M, ldo]  += gate[n] * C   (gate NULL: 1)
  *   DIT_EPI_STORE_F32 out float [M, ldo]   = C
  * A device T [M, lda], W device T [N, ldw], bias device T [N] or NULL.
- * M, N, K >= 1; K and every leading dimension a multiple of 8; lda, ldw >= K;
+ * M, N, K >= 1; K, lda and ldw multiples of 8; lda, ldw >= K;
  * ldo >= N.  tile selects the workgroup tile (0 automatic, 1: 256x256,
  * 2: 128x128, 3: 64x64; fp32 always uses 64x64). */
 enum { DIT_EPI_STORE = 0, DIT_EPI_GELU = 1, DIT_EPI_RESIDUAL = 2, DIT_EPI_STORE_F32 = 3 };
