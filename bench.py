@@ -40,7 +40,7 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "image_s_bf16"
 
-GEMM_KINDS = ("gemm_qkv", "gemm_o", "gemm_cross_q", "gemm_cross_kv", "gemm_cross_o",
+GEMM_KINDS = ("gemm_qkv_rope", "gemm_o", "gemm_cross_q", "gemm_cross_kv", "gemm_cross_o",
               "gemm_mlp1_gelu", "gemm_mlp2", "gemm_text_proj", "gemm_patch_embed", "gemm_head")
 ATTN_KINDS = ("attention_self", "attention_cross")
 
@@ -56,7 +56,7 @@ def kind_work(cfg) -> dict:
     es = 2 if cfg.dtype == "bf16" else 4
     n_lat = cfg.latent_numel
     return {
-        "gemm_qkv": ("flop", 2 * S * D * 3 * D),
+        "gemm_qkv_rope": ("flop", 2 * S * D * 3 * D),
         "gemm_o": ("flop", 2 * S * D * D),
         "gemm_cross_q": ("flop", 2 * S * D * D),
         "gemm_cross_kv": ("flop", 2 * L * D * 2 * D),
@@ -70,8 +70,6 @@ def kind_work(cfg) -> dict:
         "attention_cross": ("flop", 4 * S * L * D),
         # read the fp32 row, write the normalised row
         "layernorm_modulate": ("byte", S * D * (4 + es)),
-        # read and write q and k, read the cos/sin tables
-        "rope": ("byte", 2 * 2 * S * D * es + S * cfg.head_dim * 4),
         "patchify": ("byte", n_lat * (4 + es)),
         # read velocity tokens, read-modify-write the latents
         "unpatchify_euler": ("byte", n_lat * 4 * 3),

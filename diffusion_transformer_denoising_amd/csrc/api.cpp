@@ -137,12 +137,12 @@ dit_status hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_
 
 // Kinds of timed launches (dit_profile_* report per kind).
 enum ProfKind {
-  PK_LN = 0, PK_GEMM_QKV, PK_ROPE, PK_ATTN_SELF, PK_GEMM_O, PK_GEMM_CQ, PK_GEMM_CKV,
+  PK_LN = 0, PK_GEMM_QKV, PK_ATTN_SELF, PK_GEMM_O, PK_GEMM_CQ, PK_GEMM_CKV,
   PK_ATTN_CROSS, PK_GEMM_CO, PK_GEMM_MLP1, PK_GEMM_MLP2, PK_TIME, PK_GEMM_TXT, PK_PATCHIFY,
   PK_GEMM_PE, PK_GEMM_OUT, PK_EULER, PK_COUNT
 };
 const char *const kProfNames[PK_COUNT] = {
-    "layernorm_modulate", "gemm_qkv", "rope", "attention_self", "gemm_o", "gemm_cross_q",
+    "layernorm_modulate", "gemm_qkv_rope", "attention_self", "gemm_o", "gemm_cross_q",
     "gemm_cross_kv", "attention_cross", "gemm_cross_o", "gemm_mlp1_gelu", "gemm_mlp2",
     "time_embedding", "gemm_text_proj", "patchify", "gemm_patch_embed", "gemm_head",
     "unpatchify_euler"};
@@ -233,10 +233,12 @@ dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, cons
     a.seg_ptr[0] = q; a.seg_ld[0] = D; a.seg_trans[0] = 0;
     a.seg_ptr[1] = k; a.seg_ld[1] = D; a.seg_trans[1] = 0;
     a.seg_ptr[2] = vt; a.seg_ld[2] = p.S_pad; a.seg_trans[2] = 1;
+    // RoPE on q and k inside the projection's epilogue
+    a.seg_rope[0] = 1; a.seg_rope[1] = 1;
+    a.rope_cos = m->buf<float>(p.cos_t); a.rope_sin = m->buf<float>(p.sin_t);
+    a.rope_half_d = c.head_dim / 2;
     DIT_RUN(m, PK_GEMM_QKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
   }
-  DIT_RUN(m, PK_ROPE, s, launch_rope(m->dt, q, k, D, S, c.heads, c.head_dim, m->buf<float>(p.cos_t),
-                      m->buf<float>(p.sin_t), s));
   {
     AttnArgs a{q, D, k, D, vt, p.S_pad, o, D, S, S, c.heads, c.head_dim, scale_log2};
     DIT_RUN(m, PK_ATTN_SELF, s, launch_attention(m->dt, a, s));

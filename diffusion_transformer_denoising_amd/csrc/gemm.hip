@@ -13,8 +13,6 @@
 // so the fragment reads of 16 consecutive rows hit distinct banks) and
 // prefetches the next slice into registers while the current one feeds the
 // MFMAs, so one barrier per K step suffices.
-#include <cmath>
-
 #include "device.h"
 #include "kernels.h"
 
@@ -190,68 +188,156 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     });
   }
 
-  // ---- epilogue: lane holds column (lane & 31), rows j*8 + (lane>>5)*4 + i
+  // ---- epilogue, one 32-row strip of the wave's tile at a time, through LDS:
+  // the accumulators (lane = column, 16 rows) are written to a per-wave strip
+  // with the bias / GELU / gate applied, then read back as 8-column runs of
+  // one row, so every global access is a 16-byte (or 32-byte) vector and the
+  // fp32 residual read-modify-write is fully coalesced.  RoPE (split store
+  // segments flagged for it) rotates the (2j, 2j+1) pairs of a run in fp32
+  // before rounding.  A transposed segment is written to the strip
+  // transposed, so each output row (one column of C) gets 16-byte runs of
+  // consecutive tokens.
+  __syncthreads();  // every wave is done with the main-loop buffers
+  constexpr int SROW = WN + 4;       // fp32 strip row stride
+  constexpr int TROW = 32 + 16 / sizeof(T);  // transposed strip row stride (elements)
+  static_assert(4 * 32 * SROW * 4 <= (int)sizeof(lds), "strip does not fit");
+  float *strip = reinterpret_cast<float *>(&lds[0][0]) + wave * (32 * SROW);
+  T *stripT = reinterpret_cast<T *>(strip);
   const T *bias = static_cast<const T *>(p.bias);
+  const int colbase = n0 + wn * WN;
+  int seg = 0, segc = colbase, trans = 0, rope = 0;
+  void *dst = p.out;
+  int64_t ld = p.ldo;
+  if constexpr (EPI == EPI_SPLIT) {
+    seg = colbase / p.seg_width;  // a strip never straddles segments
+    segc = colbase - seg * p.seg_width;
+    trans = p.seg_trans[seg];
+    rope = p.seg_rope[seg];
+    dst = p.seg_ptr[seg];
+    ld = p.seg_ld[seg];
+  }
+  constexpr int VE = EPI == EPI_RESIDUAL || EPI == EPI_STORE_F32 || sizeof(T) == 4 ? 4 : 8;
+  const bool vec_ok = (ld % VE) == 0;
+
 #pragma unroll
-  for (int b = 0; b < TN; ++b) {
-    const int col = n0 + wn * WN + b * 32 + (lane & 31);
-    if (col >= N) continue;
-    const float bv = bias ? to_f32(bias[col]) : 0.0f;
-    float gv = 1.0f;
-    if constexpr (EPI == EPI_RESIDUAL) gv = p.gate ? p.gate[col] : 1.0f;
-    int seg = 0, sc = col;
-    if constexpr (EPI == EPI_SPLIT) {
-      seg = col / p.seg_width;
-      sc = col - seg * p.seg_width;
-    }
+  for (int a = 0; a < TM; ++a) {
+    const int rowbase = m0 + wm * WM + a * 32;
+    // 1. accumulators -> strip
 #pragma unroll
-    for (int a = 0; a < TM; ++a) {
+    for (int b = 0; b < TN; ++b) {
+      const int sc = b * 32 + (lane & 31);
+      const int col = colbase + sc;
+      const float bv = (bias && col < N) ? to_f32(bias[col]) : 0.0f;
+      float gv = 1.0f;
+      if constexpr (EPI == EPI_RESIDUAL) gv = (p.gate && col < N) ? p.gate[col] : 1.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row0 = m0 + wm * WM + a * 32 + j * 8 + (lane >> 5) * 4;
-        if constexpr (EPI == EPI_SPLIT) {
-          if (p.seg_trans[seg]) {
-            T *dst = static_cast<T *>(p.seg_ptr[seg]) + (int64_t)sc * p.seg_ld[seg] + row0;
-            if (row0 + 3 < M) {
-              if constexpr (sizeof(T) == 2) {
-                bf16x4 v4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v4[i] = (bf16)(acc[a][b][j * 4 + i] + bv);
-                *reinterpret_cast<bf16x4 *>(dst) = v4;
-              } else {
-                f32x4 v4;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v4[i] = acc[a][b][j * 4 + i] + bv;
-                *reinterpret_cast<f32x4 *>(dst) = v4;
-              }
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (row0 + i < M) dst[i] = from_f32<T>(acc[a][b][j * 4 + i] + bv);
-            }
-            continue;
-          }
-        }
+        const int r0 = j * 8 + (lane >> 5) * 4;
+        float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = row0 + i;
-          if (row >= M) continue;
-          const float v = acc[a][b][j * 4 + i] + bv;
-          if constexpr (EPI == EPI_STORE) {
-            static_cast<T *>(p.out)[(int64_t)row * p.ldo + col] = from_f32<T>(v);
-          } else if constexpr (EPI == EPI_GELU) {
-            static_cast<T *>(p.out)[(int64_t)row * p.ldo + col] = from_f32<T>(gelu_tanh(v));
-          } else if constexpr (EPI == EPI_RESIDUAL) {
-            float *o = static_cast<float *>(p.out) + (int64_t)row * p.ldo + col;
-            *o = *o + gv * v;
-          } else if constexpr (EPI == EPI_STORE_F32) {
-            static_cast<float *>(p.out)[(int64_t)row * p.ldo + col] = v;
+          v[i] = acc[a][b][j * 4 + i] + bv;
+          if constexpr (EPI == EPI_GELU) v[i] = gelu_tanh(v[i]);
+          if constexpr (EPI == EPI_RESIDUAL) v[i] *= gv;
+        }
+        if (EPI == EPI_SPLIT && trans) {
+          if constexpr (sizeof(T) == 2) {
+            bf16x4 t4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t4[i] = (bf16)v[i];
+            *reinterpret_cast<bf16x4 *>(stripT + sc * TROW + r0) = t4;
           } else {
-            static_cast<T *>(p.seg_ptr[seg])[(int64_t)row * p.seg_ld[seg] + sc] = from_f32<T>(v);
+            f32x4 t4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t4[i] = v[i];
+            *reinterpret_cast<f32x4 *>(stripT + sc * TROW + r0) = t4;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) strip[(r0 + i) * SROW + sc] = v[i];
+        }
+      }
+    }
+    __syncthreads();
+    // 2. strip -> global, 8-element runs
+    if (EPI == EPI_SPLIT && trans) {
+      // row c of the transposed strip = column segc + c of C = output row
+      for (int u = lane; u < WN * 4; u += 64) {
+        const int c = u >> 2, rr = (u & 3) * 8;
+        const int row = rowbase + rr;
+        if (row >= M) continue;  // runs past M stay inside the padded rows
+        T *o = static_cast<T *>(dst) + (int64_t)(segc + c) * ld + row;
+        const T *srcp = stripT + c * TROW + rr;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<U128 *>(o) = *reinterpret_cast<const U128 *>(srcp);
+        } else {
+          *reinterpret_cast<f32x4 *>(o) = *reinterpret_cast<const f32x4 *>(srcp);
+          *reinterpret_cast<f32x4 *>(o + 4) = *reinterpret_cast<const f32x4 *>(srcp + 4);
+        }
+      }
+    } else {
+      constexpr int UPR = WN / 8;  // 8-column runs per strip row
+      for (int u = lane; u < 32 * UPR; u += 64) {
+        const int r = u / UPR, c8 = (u % UPR) * 8;
+        const int row = rowbase + r, col = colbase + c8;
+        if (row >= M || col >= N) continue;
+        const int ocol = EPI == EPI_SPLIT ? segc + c8 : col;  // column in the destination
+        const float *sp = strip + r * SROW + c8;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(sp);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(sp + 4);
+        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (EPI == EPI_SPLIT && rope) {
+          // pairs (2j, 2j+1) of the head; table column = channel / 2
+          const int ch0 = (segc + c8) % (2 * p.rope_half_d);
+          const float *ct = p.rope_cos + (int64_t)row * p.rope_half_d + ch0 / 2;
+          const float *st = p.rope_sin + (int64_t)row * p.rope_half_d + ch0 / 2;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float cs = ct[q], sn = st[q];
+            const float u0 = v[2 * q], u1 = v[2 * q + 1];
+            v[2 * q] = u0 * cs - u1 * sn;
+            v[2 * q + 1] = u0 * sn + u1 * cs;
+          }
+        }
+        const int nvalid = N - col < 8 ? N - col : 8;
+        if constexpr (EPI == EPI_RESIDUAL) {
+          float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
+          if (vec_ok && nvalid == 8) {
+            f32x4 x0 = *reinterpret_cast<f32x4 *>(o), x1 = *reinterpret_cast<f32x4 *>(o + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x0[e] += v[e]; x1[e] += v[4 + e]; }
+            *reinterpret_cast<f32x4 *>(o) = x0;
+            *reinterpret_cast<f32x4 *>(o + 4) = x1;
+          } else {
+            for (int e = 0; e < nvalid; ++e) o[e] = o[e] + v[e];
+          }
+        } else if constexpr (EPI == EPI_STORE_F32) {
+          float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
+          if (vec_ok && nvalid == 8) {
+            *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          } else {
+            for (int e = 0; e < nvalid; ++e) o[e] = v[e];
+          }
+        } else {
+          T *o = static_cast<T *>(dst) + (int64_t)row * ld + ocol;
+          if (vec_ok && nvalid == 8) {
+            if constexpr (sizeof(T) == 2) {
+              bf16x8 t8;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) t8[e] = (bf16)v[e];
+              *reinterpret_cast<bf16x8 *>(o) = t8;
+            } else {
+              *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+              *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            }
+          } else {
+            for (int e = 0; e < nvalid; ++e) o[e] = from_f32<T>(v[e]);
           }
         }
       }
     }
+    __syncthreads();  // the strip is rewritten by the next pass
   }
 }
 
@@ -275,20 +361,14 @@ bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) 
   return (M + 256) * lda * es < lim && (N + 256) * ldw * es < lim;
 }
 
-// Tile choice: estimated time = (rounds of workgroups over the chip) x (tile
-// area / relative efficiency of that tile), with workgroups per CU set by LDS.
+// Tile choice (measured on MI355X): 256x256 once the grid has at least half
+// a tile per CU, else 128x128 with at least one tile per CU, else 64x64.
 static int pick_tile(int M, int N) {
-  struct C { int id, bm, bn, per_cu; double eff; };
-  const C cand[] = {{1, 256, 256, 1, 1.0}, {2, 128, 128, 2, 0.55}, {3, 64, 64, 4, 0.25}};
-  int best = 3;
-  double best_t = 1e300;
-  for (const C &c : cand) {
-    const double tiles = (double)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    const double rounds = std::ceil(tiles / (256.0 * c.per_cu));
-    const double t = rounds * c.per_cu * (double)c.bm * c.bn / c.eff;
-    if (t < best_t) { best_t = t; best = c.id; }
-  }
-  return best;
+  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+  if (t256 >= 128) return 1;
+  if (t128 >= 256) return 2;
+  return 3;
 }
 
 hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile) {
@@ -296,6 +376,8 @@ hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s,
   if (!gemm_offsets_fit(dt, a.M, a.lda, a.N, a.ldw)) return hipErrorInvalidValue;
   if (dt == DT_BF16) {
     if (tile == 0) tile = pick_tile(a.M, a.N);
+    // a split store needs every wave's column strip inside one segment
+    while (epi == EPI_SPLIT && tile < 3 && a.seg_width % (tile == 1 ? 128 : 64) != 0) ++tile;
     switch (tile) {
       case 1: return launch_t<bf16, 256, 256>(epi, a, s);
       case 2: return launch_t<bf16, 128, 128>(epi, a, s);

@@ -16,7 +16,10 @@ enum Epilogue {
   EPI_STORE_F32 = 3, // out float [M, ldo]        = C
   EPI_SPLIT = 4,     // column segment s = col / seg_width goes to seg_ptr[s]:
                      // row-major [M, seg_ld] or, when seg_trans[s], transposed
-                     // [seg_width, seg_ld] (element (row, c) at c * seg_ld + row)
+                     // [seg_width, seg_ld] (element (row, c) at c * seg_ld + row;
+                     // rows are written in runs of 8, so seg_ld must cover M
+                     // rounded up to 8); segments flagged seg_rope get the
+                     // interleaved rotary rotation with the given tables
 };
 
 struct GemmArgs {
@@ -29,10 +32,13 @@ struct GemmArgs {
   void *out;
   int64_t ldo;
   const float *gate;  // EPI_RESIDUAL
-  int seg_width;      // EPI_SPLIT
+  int seg_width;      // EPI_SPLIT (a multiple of 32)
   void *seg_ptr[3];
   int64_t seg_ld[3];
   int seg_trans[3];
+  int seg_rope[3];    // rotate (2j, 2j+1) column pairs of this segment
+  const float *rope_cos, *rope_sin;  // [M, rope_half_d] tables, per head
+  int rope_half_d;
 };
 // tile: 0 automatic, 1 256x256, 2 128x128, 3 64x64 (bf16); fp32 uses 64x64.
 hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile = 0);
@@ -59,11 +65,6 @@ hipError_t launch_attention(DType dt, const AttnArgs &a, hipStream_t s);
 // y[r, :] = LN(x[r, :]) * (1 + scale) + shift  (plain LN when shift == scale == NULL)
 hipError_t launch_ln_modulate(DType dt, const float *x, int rows, int D, float eps,
                               const float *shift, const float *scale, void *y, hipStream_t s);
-
-// In-place interleaved rotary rotation of q and k rows [S, ld] with tables
-// cos/sin [S, head_dim/2] (shared by all heads).
-hipError_t launch_rope(DType dt, void *q, void *k, int64_t ld, int S, int heads, int head_dim,
-                       const float *cos_t, const float *sin_t, hipStream_t s);
 
 // cos/sin [S, head_dim/2] for the patch grid (gf, gh, gw) and split (rf, rh, rw).
 hipError_t launch_rope_tables(float *cos_t, float *sin_t, int gf, int gh, int gw, int head_dim,

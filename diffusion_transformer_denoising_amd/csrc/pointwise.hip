@@ -88,51 +88,7 @@ hipError_t launch_ln_modulate(DType dt, const float *x, int rows, int D, float e
 }
 
 // ---------------------------------------------------------------------------
-// Rotary embedding.  Pair (2j, 2j+1) of every head is rotated by the angle of
-// table column j of the token; one thread per (token, head, pair), q and k in
-// the same pass.
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void rope_kernel(T *__restrict__ q, T *__restrict__ k, int64_t ld,
-                                                   int S, int heads, int half_d,
-                                                   const float *__restrict__ cos_t,
-                                                   const float *__restrict__ sin_t) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)S * heads * half_d;
-  if (idx >= total) return;
-  const int j = (int)(idx % half_d);
-  const int64_t th = idx / half_d;
-  const int h = (int)(th % heads);
-  const int tok = (int)(th / heads);
-  const float c = cos_t[(int64_t)tok * half_d + j];
-  const float sn = sin_t[(int64_t)tok * half_d + j];
-  const int64_t off = (int64_t)tok * ld + (int64_t)h * 2 * half_d + 2 * j;
-  {
-    const float u0 = to_f32(q[off]), u1 = to_f32(q[off + 1]);
-    q[off] = from_f32<T>(u0 * c - u1 * sn);
-    q[off + 1] = from_f32<T>(u0 * sn + u1 * c);
-  }
-  {
-    const float u0 = to_f32(k[off]), u1 = to_f32(k[off + 1]);
-    k[off] = from_f32<T>(u0 * c - u1 * sn);
-    k[off + 1] = from_f32<T>(u0 * sn + u1 * c);
-  }
-}
-
-hipError_t launch_rope(DType dt, void *q, void *k, int64_t ld, int S, int heads, int head_dim,
-                       const float *cos_t, const float *sin_t, hipStream_t s) {
-  const int64_t total = (int64_t)S * heads * (head_dim / 2);
-  if (total <= 0) return hipSuccess;
-  dim3 grid((unsigned)((total + 255) / 256));
-  if (dt == DT_BF16)
-    rope_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<bf16 *>(q), static_cast<bf16 *>(k), ld, S,
-                                           heads, head_dim / 2, cos_t, sin_t);
-  else
-    rope_kernel<float><<<grid, 256, 0, s>>>(static_cast<float *>(q), static_cast<float *>(k), ld,
-                                            S, heads, head_dim / 2, cos_t, sin_t);
-  return hipGetLastError();
-}
-
+// Rotary tables (the rotation itself runs in the QKV projection's epilogue).
 // Tables in double precision, rounded once: column j < rf/2 belongs to axis f
 // (pair j), then rh/2 columns of axis h, then rw/2 of axis w; the angle is
 // pos_axis * theta^(-2 j_axis / r_axis).
