@@ -2,17 +2,23 @@
 //
 // C[M, N] = A[M, K] * W[N, K]^T + bias, both operands K-contiguous (the
 // row-major [out, in] weight layout), fp32 accumulation on the matrix cores,
-// then one of the epilogues of kernels.h applied in registers: bias, GELU,
-// gate * (.) added into the fp32 residual stream, fp32 store, or a split
-// store that routes column segments to separate buffers (optionally
-// transposed, which is how the attention values are laid out).
+// then one epilogue (kernels.h): bias, GELU, gate * (.) added into the fp32
+// residual stream, fp32 store, or a split store that routes column segments
+// to separate buffers (transposed for the attention values, rotated by RoPE
+// for q and k).
 //
-// Tiling: a 256-thread workgroup (4 waves as 2 x 2) owns a BM x BN output
-// tile; each wave owns (BM/2) x (BN/2) as 32x32 MFMA tiles.  The K loop
-// stages 128-byte slices of A and W rows through LDS (one 16-byte pad per row
-// so the fragment reads of 16 consecutive rows hit distinct banks) and
-// prefetches the next slice into registers while the current one feeds the
-// MFMAs, so one barrier per K step suffices.
+// A 256-thread workgroup (4 waves as 2 x 2) owns a BM x BN output tile; each
+// wave owns (BM/2) x (BN/2) as 32x32 MFMA tiles.  Two main loops:
+//   gemm_kernel (256x256 bf16, 64x64 fp32): 128-byte K slices staged through
+//     registers into double-buffered, row-padded LDS; the instruction order
+//     of a K step is pinned (sched_group_barrier) so fragment reads, staging
+//     stores and global loads interleave with the MFMAs, with the barrier
+//     before the last chunk.
+//   gemm_dl_kernel (64x64, 128x128 bf16): K slices move global -> LDS
+//     directly (buffer loads with the LDS destination) into a ring of NS
+//     stages, so NS-1 slices are in flight; small problems have too few
+//     workgroups per CU to hide memory latency any other way.
+// Both share the LDS-staged epilogue (gemm_epilogue).
 #include "device.h"
 #include "kernels.h"
 
@@ -43,8 +49,195 @@ __device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_bit_cast(U128, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes lds_block + 16 i (lds_block is wave-uniform).
+__device__ __forceinline__ void gemm_lds_load16(__amdgpu_buffer_rsrc_t r, void *lds_block,
+                                                uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_block, 16,
+                                           voff, 0, 0, 0);
+}
+
 constexpr uint32_t OOB = 0x80000000u;  // an offset past every operand (sizes < 2^31 bytes)
 
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left open).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
+
+// Order this wave's LDS writes before its later LDS reads (other lanes' data).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue, one 32-row strip of the wave's tile at a time, through the wave's
+// own LDS region: phase 1 writes the accumulators (lane = column, 16 rows)
+// with bias / GELU / gate applied; phase 2 reads them back as 8-column runs
+// of one row, so every global access is a 16-byte (or 32-byte) vector and the
+// fp32 residual read-modify-write is coalesced.  RoPE (split segments flagged
+// for it) rotates the (2j, 2j+1) pairs of a run in fp32 before rounding.  A
+// transposed segment goes through a transposed strip, so each output row
+// (one column of C) gets 16-byte runs of consecutive tokens.
+// The caller has synchronised the workgroup: scratch is free LDS of at least
+// 4 * gemm_strip_floats<...>() floats.
+// ---------------------------------------------------------------------------
+template <typename T, int WN>
+constexpr int gemm_strip_floats() {
+  constexpr int SROW = WN + 4, TROW = 32 + 16 / (int)sizeof(T);
+  return (32 * SROW * 4 > WN * TROW * (int)sizeof(T) ? 32 * SROW * 4 : WN * TROW * (int)sizeof(T)) / 4;
+}
+
+template <typename T, int BM, int BN, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, f32x16 (&acc)[BM / 64][BN / 64],
+                                              float *scratch, int m0, int n0) {
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int SROW = WN + 4;                        // fp32 strip row stride
+  constexpr int TROW = 32 + 16 / (int)sizeof(T);      // transposed strip row stride
+  constexpr int REG = gemm_strip_floats<T, WN>();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int M = p.M, N = p.N;
+  float *strip = scratch + wave * REG;
+  T *stripT = reinterpret_cast<T *>(strip);
+  const T *bias = static_cast<const T *>(p.bias);
+  const int colbase = n0 + wn * WN;
+  int segc = colbase, trans = 0, rope = 0;
+  void *dst = p.out;
+  int64_t ld = p.ldo;
+  if constexpr (EPI == EPI_SPLIT) {
+    const int seg = colbase / p.seg_width;  // a strip never straddles segments
+    segc = colbase - seg * p.seg_width;
+    trans = p.seg_trans[seg];
+    rope = p.seg_rope[seg];
+    dst = p.seg_ptr[seg];
+    ld = p.seg_ld[seg];
+  }
+  constexpr int VE = EPI == EPI_RESIDUAL || EPI == EPI_STORE_F32 || sizeof(T) == 4 ? 4 : 8;
+  const bool vec_ok = (ld % VE) == 0;
+
+#pragma unroll
+  for (int a = 0; a < TM; ++a) {
+    const int rowbase = m0 + wm * WM + a * 32;
+    // 1. accumulators -> strip
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      const int sc = b * 32 + (lane & 31);
+      const int col = colbase + sc;
+      const float bv = (bias && col < N) ? to_f32(bias[col]) : 0.0f;
+      float gv = 1.0f;
+      if constexpr (EPI == EPI_RESIDUAL) gv = (p.gate && col < N) ? p.gate[col] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = j * 8 + (lane >> 5) * 4;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = acc[a][b][j * 4 + i] + bv;
+          if constexpr (EPI == EPI_GELU) v[i] = gelu_tanh(v[i]);
+          if constexpr (EPI == EPI_RESIDUAL) v[i] *= gv;
+        }
+        if (EPI == EPI_SPLIT && trans) {
+          if constexpr (sizeof(T) == 2) {
+            bf16x4 t4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t4[i] = (bf16)v[i];
+            *reinterpret_cast<bf16x4 *>(stripT + sc * TROW + r0) = t4;
+          } else {
+            *reinterpret_cast<f32x4 *>(stripT + sc * TROW + r0) = f32x4{v[0], v[1], v[2], v[3]};
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) strip[(r0 + i) * SROW + sc] = v[i];
+        }
+      }
+    }
+    wave_lds_sync();
+    // 2. strip -> global, 8-element runs
+    if (EPI == EPI_SPLIT && trans) {
+      // row c of the transposed strip = column segc + c of C = output row
+      for (int u = lane; u < WN * 4; u += 64) {
+        const int c = u >> 2, rr = (u & 3) * 8;
+        const int row = rowbase + rr;
+        if (row >= M) continue;  // runs past M stay inside the padded rows
+        T *o = static_cast<T *>(dst) + (int64_t)(segc + c) * ld + row;
+        const T *srcp = stripT + c * TROW + rr;
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<U128 *>(o) = *reinterpret_cast<const U128 *>(srcp);
+        } else {
+          *reinterpret_cast<f32x4 *>(o) = *reinterpret_cast<const f32x4 *>(srcp);
+          *reinterpret_cast<f32x4 *>(o + 4) = *reinterpret_cast<const f32x4 *>(srcp + 4);
+        }
+      }
+    } else {
+      constexpr int UPR = WN / 8;  // 8-column runs per strip row
+      for (int u = lane; u < 32 * UPR; u += 64) {
+        const int r = u / UPR, c8 = (u % UPR) * 8;
+        const int row = rowbase + r, col = colbase + c8;
+        if (row >= M || col >= N) continue;
+        const int ocol = EPI == EPI_SPLIT ? segc + c8 : col;  // column in the destination
+        const float *sp = strip + r * SROW + c8;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(sp);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(sp + 4);
+        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (EPI == EPI_SPLIT && rope) {
+          // pairs (2j, 2j+1) of the head; table column = channel / 2
+          const int ch0 = (segc + c8) % (2 * p.rope_half_d);
+          const float *ct = p.rope_cos + (int64_t)row * p.rope_half_d + ch0 / 2;
+          const float *st = p.rope_sin + (int64_t)row * p.rope_half_d + ch0 / 2;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float cs = ct[q], sn = st[q];
+            const float u0 = v[2 * q], u1 = v[2 * q + 1];
+            v[2 * q] = u0 * cs - u1 * sn;
+            v[2 * q + 1] = u0 * sn + u1 * cs;
+          }
+        }
+        const int nvalid = N - col < 8 ? N - col : 8;
+        if constexpr (EPI == EPI_RESIDUAL) {
+          float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
+          if (vec_ok && nvalid == 8) {
+            f32x4 x0 = *reinterpret_cast<f32x4 *>(o), x1 = *reinterpret_cast<f32x4 *>(o + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x0[e] += v[e]; x1[e] += v[4 + e]; }
+            *reinterpret_cast<f32x4 *>(o) = x0;
+            *reinterpret_cast<f32x4 *>(o + 4) = x1;
+          } else {
+            for (int e = 0; e < nvalid; ++e) o[e] = o[e] + v[e];
+          }
+        } else if constexpr (EPI == EPI_STORE_F32) {
+          float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
+          if (vec_ok && nvalid == 8) {
+            *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+          } else {
+            for (int e = 0; e < nvalid; ++e) o[e] = v[e];
+          }
+        } else {
+          T *o = static_cast<T *>(dst) + (int64_t)row * ld + ocol;
+          if (vec_ok && nvalid == 8) {
+            if constexpr (sizeof(T) == 2) {
+              bf16x8 t8;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) t8[e] = (bf16)v[e];
+              *reinterpret_cast<bf16x8 *>(o) = t8;
+            } else {
+              *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+              *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            }
+          } else {
+            for (int e = 0; e < nvalid; ++e) o[e] = from_f32<T>(v[e]);
+          }
+        }
+      }
+    }
+    wave_lds_sync();  // the strip is rewritten by the next pass
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged main loop (256x256 bf16; 64x64 fp32).
+// ---------------------------------------------------------------------------
 template <typename T, int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   constexpr int BK = 128 / sizeof(T);   // elements in a 128-byte row slice
@@ -58,6 +251,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   typedef typename Frag<T>::type F;
 
   __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * ROW];
+  static_assert(4 * gemm_strip_floats<T, WN>() * 4 <= (int)sizeof(lds), "epilogue strips");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -188,157 +382,100 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     });
   }
 
-  // ---- epilogue, one 32-row strip of the wave's tile at a time, through LDS:
-  // the accumulators (lane = column, 16 rows) are written to a per-wave strip
-  // with the bias / GELU / gate applied, then read back as 8-column runs of
-  // one row, so every global access is a 16-byte (or 32-byte) vector and the
-  // fp32 residual read-modify-write is fully coalesced.  RoPE (split store
-  // segments flagged for it) rotates the (2j, 2j+1) pairs of a run in fp32
-  // before rounding.  A transposed segment is written to the strip
-  // transposed, so each output row (one column of C) gets 16-byte runs of
-  // consecutive tokens.
-  __syncthreads();  // every wave is done with the main-loop buffers
-  constexpr int SROW = WN + 4;       // fp32 strip row stride
-  constexpr int TROW = 32 + 16 / sizeof(T);  // transposed strip row stride (elements)
-  static_assert(4 * 32 * SROW * 4 <= (int)sizeof(lds), "strip does not fit");
-  float *strip = reinterpret_cast<float *>(&lds[0][0]) + wave * (32 * SROW);
-  T *stripT = reinterpret_cast<T *>(strip);
-  const T *bias = static_cast<const T *>(p.bias);
-  const int colbase = n0 + wn * WN;
-  int seg = 0, segc = colbase, trans = 0, rope = 0;
-  void *dst = p.out;
-  int64_t ld = p.ldo;
-  if constexpr (EPI == EPI_SPLIT) {
-    seg = colbase / p.seg_width;  // a strip never straddles segments
-    segc = colbase - seg * p.seg_width;
-    trans = p.seg_trans[seg];
-    rope = p.seg_rope[seg];
-    dst = p.seg_ptr[seg];
-    ld = p.seg_ld[seg];
-  }
-  constexpr int VE = EPI == EPI_RESIDUAL || EPI == EPI_STORE_F32 || sizeof(T) == 4 ? 4 : 8;
-  const bool vec_ok = (ld % VE) == 0;
 
+  __syncthreads();  // every wave is done with the main-loop buffers
+  gemm_epilogue<T, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0);
+}
+
+// ---------------------------------------------------------------------------
+// Direct-to-LDS main loop with an NS-stage ring (bf16, BM x BN up to 128).
+// Stage layout: BM rows of A then BN rows of W, 128 bytes (64 k) each; the
+// 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), which makes
+// the fragment reads of 16 consecutive rows conflict-free while every wave
+// load instruction still writes one contiguous 1 KB block (8 rows).
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int NS, int EPI>
+__global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
+  typedef bf16x8 F;
+  constexpr int BK = 64, ROWB = 128;
+  constexpr int STAGE = (BM + BN) * ROWB;        // bytes per stage
+  constexpr int IPS = (BM + BN) / 32;            // load instructions per wave per stage
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  static_assert((NS - 2) * IPS < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+  static_assert(4 * gemm_strip_floats<bf16, WN>() * 4 <= NS * STAGE, "epilogue strips");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int M = p.M, N = p.N, K = p.K;
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.A, (uint32_t)((int64_t)M * p.lda * 2));
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.W, (uint32_t)((int64_t)N * p.ldw * 2));
+
+  // Load instruction j of this wave fills stage rows j*32 + wave*8 .. +7; lane
+  // i moves physical chunk i & 7 of row j*32 + wave*8 + (i >> 3).
+  const int prow = wave * 8 + (lane >> 3);           // row within each 32-row group
+  const int logical = (lane & 7) ^ ((prow >> 1) & 7); // logical 16-byte chunk it carries
+  uint32_t src[IPS];
 #pragma unroll
-  for (int a = 0; a < TM; ++a) {
-    const int rowbase = m0 + wm * WM + a * 32;
-    // 1. accumulators -> strip
-#pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const int sc = b * 32 + (lane & 31);
-      const int col = colbase + sc;
-      const float bv = (bias && col < N) ? to_f32(bias[col]) : 0.0f;
-      float gv = 1.0f;
-      if constexpr (EPI == EPI_RESIDUAL) gv = (p.gate && col < N) ? p.gate[col] : 1.0f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r0 = j * 8 + (lane >> 5) * 4;
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = acc[a][b][j * 4 + i] + bv;
-          if constexpr (EPI == EPI_GELU) v[i] = gelu_tanh(v[i]);
-          if constexpr (EPI == EPI_RESIDUAL) v[i] *= gv;
-        }
-        if (EPI == EPI_SPLIT && trans) {
-          if constexpr (sizeof(T) == 2) {
-            bf16x4 t4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t4[i] = (bf16)v[i];
-            *reinterpret_cast<bf16x4 *>(stripT + sc * TROW + r0) = t4;
-          } else {
-            f32x4 t4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t4[i] = v[i];
-            *reinterpret_cast<f32x4 *>(stripT + sc * TROW + r0) = t4;
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) strip[(r0 + i) * SROW + sc] = v[i];
-        }
-      }
-    }
-    __syncthreads();
-    // 2. strip -> global, 8-element runs
-    if (EPI == EPI_SPLIT && trans) {
-      // row c of the transposed strip = column segc + c of C = output row
-      for (int u = lane; u < WN * 4; u += 64) {
-        const int c = u >> 2, rr = (u & 3) * 8;
-        const int row = rowbase + rr;
-        if (row >= M) continue;  // runs past M stay inside the padded rows
-        T *o = static_cast<T *>(dst) + (int64_t)(segc + c) * ld + row;
-        const T *srcp = stripT + c * TROW + rr;
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<U128 *>(o) = *reinterpret_cast<const U128 *>(srcp);
-        } else {
-          *reinterpret_cast<f32x4 *>(o) = *reinterpret_cast<const f32x4 *>(srcp);
-          *reinterpret_cast<f32x4 *>(o + 4) = *reinterpret_cast<const f32x4 *>(srcp + 4);
-        }
-      }
-    } else {
-      constexpr int UPR = WN / 8;  // 8-column runs per strip row
-      for (int u = lane; u < 32 * UPR; u += 64) {
-        const int r = u / UPR, c8 = (u % UPR) * 8;
-        const int row = rowbase + r, col = colbase + c8;
-        if (row >= M || col >= N) continue;
-        const int ocol = EPI == EPI_SPLIT ? segc + c8 : col;  // column in the destination
-        const float *sp = strip + r * SROW + c8;
-        const f32x4 lo = *reinterpret_cast<const f32x4 *>(sp);
-        const f32x4 hi = *reinterpret_cast<const f32x4 *>(sp + 4);
-        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if (EPI == EPI_SPLIT && rope) {
-          // pairs (2j, 2j+1) of the head; table column = channel / 2
-          const int ch0 = (segc + c8) % (2 * p.rope_half_d);
-          const float *ct = p.rope_cos + (int64_t)row * p.rope_half_d + ch0 / 2;
-          const float *st = p.rope_sin + (int64_t)row * p.rope_half_d + ch0 / 2;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float cs = ct[q], sn = st[q];
-            const float u0 = v[2 * q], u1 = v[2 * q + 1];
-            v[2 * q] = u0 * cs - u1 * sn;
-            v[2 * q + 1] = u0 * sn + u1 * cs;
-          }
-        }
-        const int nvalid = N - col < 8 ? N - col : 8;
-        if constexpr (EPI == EPI_RESIDUAL) {
-          float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
-          if (vec_ok && nvalid == 8) {
-            f32x4 x0 = *reinterpret_cast<f32x4 *>(o), x1 = *reinterpret_cast<f32x4 *>(o + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { x0[e] += v[e]; x1[e] += v[4 + e]; }
-            *reinterpret_cast<f32x4 *>(o) = x0;
-            *reinterpret_cast<f32x4 *>(o + 4) = x1;
-          } else {
-            for (int e = 0; e < nvalid; ++e) o[e] = o[e] + v[e];
-          }
-        } else if constexpr (EPI == EPI_STORE_F32) {
-          float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
-          if (vec_ok && nvalid == 8) {
-            *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
-          } else {
-            for (int e = 0; e < nvalid; ++e) o[e] = v[e];
-          }
-        } else {
-          T *o = static_cast<T *>(dst) + (int64_t)row * ld + ocol;
-          if (vec_ok && nvalid == 8) {
-            if constexpr (sizeof(T) == 2) {
-              bf16x8 t8;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) t8[e] = (bf16)v[e];
-              *reinterpret_cast<bf16x8 *>(o) = t8;
-            } else {
-              *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
-              *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
-            }
-          } else {
-            for (int e = 0; e < nvalid; ++e) o[e] = from_f32<T>(v[e]);
-          }
-        }
-      }
-    }
-    __syncthreads();  // the strip is rewritten by the next pass
+  for (int j = 0; j < IPS; ++j) {
+    const int row = j * 32 + prow;
+    src[j] = row < BM ? (uint32_t)(((int64_t)(m0 + row) * p.lda + logical * 8) * 2)
+                      : (uint32_t)(((int64_t)(n0 + row - BM) * p.ldw + logical * 8) * 2);
   }
+  auto issue = [&](int kt, int stage) {
+    const int k0 = kt * BK;
+    const bool kin = k0 + logical * 8 < K;
+    char *sb = lds + stage * STAGE + wave * 1024;
+#pragma unroll
+    for (int j = 0; j < IPS; ++j)
+      gemm_lds_load16(j * 32 < BM ? ars : wrs, sb + j * 4096, kin ? src[j] + k0 * 2 : OOB);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.0f;
+
+  const int swz = (l32 >> 1) & 7;
+  const int arow = (wm * WM + l32) * ROWB, wrow = (BM + wn * WN + l32) * ROWB;
+  F af[2][TM], wf[2][TN];
+  auto lload = [&](const char *sb, int ch, int slot) {
+    const int off = ((ch * 2 + half) ^ swz) * 16;
+#pragma unroll
+    for (int a = 0; a < TM; ++a) af[slot][a] = *reinterpret_cast<const F *>(sb + arow + a * 32 * ROWB + off);
+#pragma unroll
+    for (int b = 0; b < TN; ++b) wf[slot][b] = *reinterpret_cast<const F *>(sb + wrow + b * 32 * ROWB + off);
+  };
+
+  const int KT = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, s);
+  int stage = 0;
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPS));  // slice kt landed (this wave)
+    __syncthreads();                                          // ... and for every wave
+    const int fill = stage == 0 ? NS - 1 : stage - 1;         // the stage read last step
+    issue(kt + NS - 1, fill);
+    const char *sb = lds + stage * STAGE;
+    lload(sb, 0, 0);
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      if (ch < 3) lload(sb, ch + 1, (ch + 1) & 1);
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) mma32(af[ch & 1][a], wf[ch & 1][b], acc[a][b]);
+    }
+    stage = stage + 1 == NS ? 0 : stage + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still be landing in LDS
+  __syncthreads();
+  gemm_epilogue<bf16, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(lds), m0, n0);
 }
 
 template <typename T, int BM, int BN>
@@ -350,6 +487,20 @@ static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
     case EPI_RESIDUAL: gemm_kernel<T, BM, BN, EPI_RESIDUAL><<<grid, 256, 0, s>>>(a); break;
     case EPI_STORE_F32: gemm_kernel<T, BM, BN, EPI_STORE_F32><<<grid, 256, 0, s>>>(a); break;
     case EPI_SPLIT: gemm_kernel<T, BM, BN, EPI_SPLIT><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int NS>
+static hipError_t launch_dl(Epilogue epi, const GemmArgs &a, hipStream_t s) {
+  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+  switch (epi) {
+    case EPI_STORE: gemm_dl_kernel<BM, BN, NS, EPI_STORE><<<grid, 256, 0, s>>>(a); break;
+    case EPI_GELU: gemm_dl_kernel<BM, BN, NS, EPI_GELU><<<grid, 256, 0, s>>>(a); break;
+    case EPI_RESIDUAL: gemm_dl_kernel<BM, BN, NS, EPI_RESIDUAL><<<grid, 256, 0, s>>>(a); break;
+    case EPI_STORE_F32: gemm_dl_kernel<BM, BN, NS, EPI_STORE_F32><<<grid, 256, 0, s>>>(a); break;
+    case EPI_SPLIT: gemm_dl_kernel<BM, BN, NS, EPI_SPLIT><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -380,8 +531,8 @@ hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s,
     while (epi == EPI_SPLIT && tile < 3 && a.seg_width % (tile == 1 ? 128 : 64) != 0) ++tile;
     switch (tile) {
       case 1: return launch_t<bf16, 256, 256>(epi, a, s);
-      case 2: return launch_t<bf16, 128, 128>(epi, a, s);
-      default: return launch_t<bf16, 64, 64>(epi, a, s);
+      case 2: return launch_dl<128, 128, 4>(epi, a, s);
+      default: return launch_dl<64, 64, 5>(epi, a, s);
     }
   }
   return launch_t<float, 64, 64>(epi, a, s);
