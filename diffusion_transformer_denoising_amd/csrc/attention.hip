@@ -419,7 +419,10 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_bf16_kernel(AttnArgs p) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_T) != 0) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_T) != 0, 0)) {
+      // rare: keep it a real branch (the empty asm stops the compiler from
+      // speculating the 4*HD multiplies onto every tile)
+      asm volatile("" ::: "memory");
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
