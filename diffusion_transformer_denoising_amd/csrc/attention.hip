@@ -271,10 +271,26 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
 
 // ---------------------------------------------------------------------------
 // bf16 kernel: K and V^T tiles move global -> LDS directly (buffer loads with
-// the LDS destination, no staging registers), double-buffered in LDS, so the
-// next tile streams in while the current one feeds the MFMAs.
+// the LDS destination, no staging registers), each in its own double-buffered
+// ring, so the next tiles stream in while the current ones feed the MFMAs.
 //
-// LDS layouts (per stage), chosen for conflict-free 16-byte fragment reads:
+// Software pipeline, per wave and key tile i (64 keys):
+//   phase A: S(i+1) = K(i+1) Q^T on the matrix cores, while the vector ALU
+//            finishes P(i) = 2^x(i) (second half), packs it to bf16 and sums it;
+//   phase B: O^T += V(i)^T P(i)^T on the matrix cores, while the vector ALU
+//            forms x(i+1) = c S(i+1) - m and the first half of P(i+1);
+// so the exponentials of one tile run under the products of its neighbours
+// instead of between them.
+//
+// Running max: m is set from the first tile's exact row max and afterwards
+// only moves when a lane's partial row sum of a tile exceeds 2^16 (some
+// score rose ~16 log2 units above m), tested once per tile after phase A.
+// That rare path finds the tile's row max, rescales O and the running sum,
+// and recomputes P(i); otherwise p <= 2^16 keeps every value finite in fp32
+// and bf16.  Row sums accumulate the bf16 P values (the very numbers the
+// P.V product uses) with bf16 dot-2 instructions.
+//
+// LDS layouts, chosen for conflict-free 16-byte fragment reads:
 //   K    [64 rows][HD]: row m holds key sigma(m) of the tile, where sigma
 //        swaps bits 2 and 3 of m; 16-byte chunk c of row m is stored at chunk
 //        c ^ kswz(m).  The row permutation makes the P fragment of lane half
@@ -302,6 +318,26 @@ __device__ __forceinline__ int att_kswz(int row) {
   return (row / RP) % KCH;
 }
 
+// p = 2^x for the 16 scores of one 32-key half tile -> two bf16 P chunks;
+// their sum (of the rounded values) is added to l.
+__device__ __forceinline__ void att_exp_half(const f32x16 &x, bf16x8 &lo, bf16x8 &hi, float &l) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lo[e] = (bf16)fast_exp2(x[e]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hi[e] = (bf16)fast_exp2(x[8 + e]);
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2 pr = {lo[2 * k], lo[2 * k + 1]};
+    l = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l, false);
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16x2 pr = {hi[2 * k], hi[2 * k + 1]};
+    l = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l, false);
+  }
+}
+
 template <int HD, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void attention_bf16_kernel(AttnArgs p) {
   typedef bf16x8 F;
@@ -309,17 +345,24 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_bf16_kernel(AttnArgs p) 
   constexpr int KCHUNK = KROWB / 16;       // 16-byte chunks per K row
   constexpr int KBYTES = ATT_BK * KROWB;   // K tile
   constexpr int VBYTES = HD * ATT_BK * 2;  // V^T tile (rows of 128 bytes)
-  constexpr int STAGE = KBYTES + VBYTES;
   constexpr int KPIECES = KBYTES / 16, VPIECES = VBYTES / 16;
   constexpr int KINSTR = KPIECES / (64 * NW), VINSTR = VPIECES / (64 * NW);
   static_assert(KINSTR >= 1 && VINSTR >= 1 && KPIECES % (64 * NW) == 0, "tile split");
   constexpr int QCH = HD / 16;
   constexpr int DT = HD / 32;
   constexpr int NT = 64 * NW;
+  constexpr int NQK = 2 * QCH;             // S MFMAs per tile
+  constexpr int NPV = 4 * DT;              // P.V MFMAs per tile
+  // vector instructions per MFMA slot: phase A has 32 (16 exp, 8 pack, 8 dot),
+  // phase B 64 (32 scale, 16 exp, 8 pack, 8 dot)
+  constexpr int VA = (32 + NQK - 1) / NQK, VB = (64 + NPV - 1) / NPV;
+  constexpr float PSUM_MAX = 65536.0f;
 
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  // [K stage 0][K stage 1][V^T stage 0][V^T stage 1]
+  __shared__ __attribute__((aligned(1024))) char lds[2 * KBYTES + 2 * VBYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int head = blockIdx.y;
   const int q0 = blockIdx.x * (32 * NW) + wave * 32;
@@ -349,14 +392,17 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_bf16_kernel(AttnArgs p) 
     voff[j] = (uint32_t)((((int64_t)head * HD + row) * p.ldv + logical * 8) * 2);
   }
   const uint32_t kstep = (uint32_t)(ATT_BK * p.ldk * 2);
-  auto issue = [&](int it, int stage) {
-    char *sbase = lds + stage * STAGE;
+  auto issue_k = [&](int it, int slot) {
+    char *b = lds + slot * KBYTES;
 #pragma unroll
     for (int j = 0; j < KINSTR; ++j)
-      lds_load16(krs, sbase + (j * NW + wave) * 1024, koff[j] + it * kstep);
+      lds_load16(krs, b + (j * NW + wave) * 1024, koff[j] + (uint32_t)it * kstep);
+  };
+  auto issue_v = [&](int it, int slot) {
+    char *b = lds + 2 * KBYTES + slot * VBYTES;
 #pragma unroll
     for (int j = 0; j < VINSTR; ++j)
-      lds_load16(vrs, sbase + KBYTES + (j * NW + wave) * 1024, voff[j] + it * (ATT_BK * 2));
+      lds_load16(vrs, b + (j * NW + wave) * 1024, voff[j] + (uint32_t)it * (ATT_BK * 2));
   };
 
   // Q fragments stay in registers for the whole key loop.
@@ -374,114 +420,199 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_bf16_kernel(AttnArgs p) 
     }
   }
 
+  // per-lane LDS byte offsets of the fragments (stage and tile row offsets
+  // are added as immediates)
+  int kaddr[QCH], vaddr[4];
+  {
+    const int kswz = att_kswz<HD>(l32), vswz = (l32 >> 1) & 7;
+#pragma unroll
+    for (int ch = 0; ch < QCH; ++ch) kaddr[ch] = l32 * KROWB + (((ch * 2 + half) ^ kswz) * 16);
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) vaddr[ch] = 2 * KBYTES + l32 * 128 + (((ch * 2 + half) ^ vswz) * 16);
+  }
+
   f32x16 o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[t][e] = 0.0f;
-  float m_run = -1e30f, l_run = 0.0f;
-  constexpr float RESCALE_T = 8.0f;
   const float c = p.scale_log2;
-  const int kswz = att_kswz<HD>(l32);
-  const int vswz = (l32 >> 1) & 7;
+  float m_run, l_run = 0.0f;
 
-  auto tile = [&](auto MASKED, int stage, int t0) {
-    constexpr bool masked = decltype(MASKED)::value;
-    const char *kb = lds + stage * STAGE + l32 * KROWB;
-    const char *vb = lds + stage * STAGE + KBYTES + l32 * 128;
-    f32x16 s[2];
+  const int n_tiles = (sk + ATT_BK - 1) / ATT_BK;
+  const bool ragged = (sk % ATT_BK) != 0;
+
+  // S^T of the tile in K stage `slot` into s (raw scores)
+  auto qk = [&](f32x16 (&s)[2], int slot) {
+    static_for<NQK>([&](auto U) {
+      constexpr int u = decltype(U)::value, ch = u >> 1, mt = u & 1;
+      const F kf = *reinterpret_cast<const F *>(lds + slot * KBYTES + kaddr[ch] + mt * 32 * KROWB);
+      if constexpr (ch == 0) {
+        f32x16 z;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[mt][e] = 0.0f;
-#pragma unroll
-    for (int ch = 0; ch < QCH; ++ch) {
-      const int off = ((ch * 2 + half) ^ kswz) * 16;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        F kf = *reinterpret_cast<const F *>(kb + mt * 32 * KROWB + off);
-        mma32(kf, qf[ch], s[mt]);
+        for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0], z, 0, 0, 0);
+      } else {
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ch], s[mt], 0, 0, 0);
       }
-    }
-    if constexpr (masked) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          // accumulator row m = (e>>2)*8 + half*4 + (e&3) holds key sigma(m)
-          const int key = t0 + mt * 32 + (e >> 3) * 16 + half * 8 + ((e >> 2) & 1) * 4 + (e & 3);
-          if (key >= sk) s[mt][e] = -INFINITY;
-        }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[mt][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(mx > m_run + RESCALE_T) != 0, 0)) {
-      // rare: keep it a real branch (the empty asm stops the compiler from
-      // speculating the 4*HD multiplies onto every tile)
-      asm volatile("" ::: "memory");
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
-    }
-    const float nm = -m_run;
+    });
+  };
+  // scores of keys at or past sk -> -inf (tile starting at key t0)
+  auto mask = [&](f32x16 (&s)[2], int t0) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float pe = fast_exp2(fmaf(s[mt][e], c, nm));
-        s[mt][e] = pe;
-        l_run += pe;
+        // accumulator row m = (e>>2)*8 + half*4 + (e&3) holds key sigma(m)
+        const int key = t0 + mt * 32 + (e >> 3) * 16 + half * 8 + ((e >> 2) & 1) * 4 + (e & 3);
+        if (key >= sk) s[mt][e] = -INFINITY;
       }
+  };
+  // the rare path: move m to the tile's row max, rescale, recompute P
+  auto rescale = [&](f32x16 (&x)[2], F (&pc)[4], float &lc) {
+    float mx = x[0][0];
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const int mt = ch >> 1, j0 = (ch & 1) * 2;
-      F pf;
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[mt][j0 * 4 + e];
-      const int off = ((ch * 2 + half) ^ vswz) * 16;
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, x[mt][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float d = fmaxf(mx, 0.0f);
+    m_run += d;
+    const float alpha = fast_exp2(-d);
+    l_run *= alpha;
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        F vf = *reinterpret_cast<const F *>(vb + t * 32 * 128 + off);
-        mma32(vf, pf, o[t]);
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[mt][e] -= d;
+    lc = 0.0f;
+    att_exp_half(x[0], pc[0], pc[1], lc);
+    att_exp_half(x[1], pc[2], pc[3], lc);
+  };
+
+  // One pipeline step: finishes tile i (P(i), O += P(i) V(i)) and, with
+  // HAS_NEXT, computes the scores and first half of P of tile i + 1.
+  // par = i & 1 selects the stages: K(i+1) in K stage par^1, V(i) in V stage par.
+  auto step = [&](auto HAS_NEXT, auto MASK_NEXT, f32x16 (&xc)[2], F (&pc)[4], float &lc,
+                  f32x16 (&xn)[2], F (&pn)[4], float &ln, const int i, const int par) {
+    constexpr bool has_next = decltype(HAS_NEXT)::value;
+    constexpr bool mask_next = decltype(MASK_NEXT)::value;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): K(i+1), V(i) landed
+    __syncthreads();                      // ... for every wave; K(i), V(i-1) free
+    if (i + 2 < n_tiles) issue_k(i + 2, par);
+    if (i + 1 < n_tiles) issue_v(i + 1, par ^ 1);
+    if constexpr (!has_next) {
+      if (ragged) {
+        // clear V^T entries of keys past the end (inside the caller's rows)
+        bf16 *vt = reinterpret_cast<bf16 *>(lds + 2 * KBYTES + par * VBYTES);
+        const int valid = sk - i * ATT_BK;
+        for (int x = tid; x < HD * ATT_BK; x += NT) {
+          const int row = x / ATT_BK, key = x % ATT_BK;
+          if (key >= valid) {
+            const int phys = (key >> 3) ^ ((row >> 1) & 7);
+            vt[row * ATT_BK + phys * 8 + (key & 7)] = (bf16)0.0f;
+          }
+        }
+        __syncthreads();
       }
+    }
+    // ---- phase A: S(i+1) on the matrix cores | second half of P(i)
+    if constexpr (has_next) qk(xn, par ^ 1);
+    att_exp_half(xc[1], pc[2], pc[3], lc);
+    if constexpr (has_next) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      static_for<NQK>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, VA, 0);
+      });
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(lc <= PSUM_MAX)) != 0, 0)) {
+      asm volatile("" ::: "memory");
+      rescale(xc, pc, lc);
+    }
+    l_run += lc;
+    // ---- phase B: O^T += V(i)^T P(i)^T | x(i+1) and first half of P(i+1)
+    static_for<NPV>([&](auto U) {
+      constexpr int u = decltype(U)::value, ch = u / DT, t = u % DT;
+      const F vf = *reinterpret_cast<const F *>(lds + par * VBYTES + vaddr[ch] + t * 32 * 128);
+      mma32(vf, pc[ch], o[t]);
+    });
+    if constexpr (has_next) {
+      const float nm = -m_run;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xn[mt][e] = fmaf(xn[mt][e], c, nm);
+      if constexpr (mask_next) mask(xn, (i + 1) * ATT_BK);
+      ln = 0.0f;
+      att_exp_half(xn[0], pn[0], pn[1], ln);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      static_for<NPV>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, VB, 0);
+      });
+      // keep this work here, under the P.V products: without the pins the
+      // compiler sinks it past the next step's barrier
+      asm volatile("" : "+v"(xn[1]), "+v"(pn[0]), "+v"(pn[1]), "+v"(ln));
     }
   };
 
-  const int n_tiles = (sk + ATT_BK - 1) / ATT_BK;
-  const int n_full = sk / ATT_BK;
-  issue(0, 0);
-  for (int it = 0; it < n_full; ++it) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this tile's loads landed
-    __syncthreads();                      // ... for every wave; other stage free
-    if (it + 1 < n_tiles) issue(it + 1, (it + 1) & 1);
-    tile(std::false_type{}, it & 1, it * ATT_BK);
+  f32x16 xa[2], xb[2];
+  F pa[4], pb[4];
+  float la = 0.0f, lb = 0.0f;
+
+  // ---- prologue: tile 0 scores, exact row max, first half of P(0)
+  issue_k(0, 0);
+  issue_v(0, 0);
+  if (n_tiles > 1) issue_k(1, 1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  qk(xa, 0);
+  if (n_tiles == 1 && ragged) mask(xa, 0);
+  {
+    float mx = xa[0][0];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, xa[mt][e]);
+    m_run = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    const float nm = -m_run;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xa[mt][e] = fmaf(xa[mt][e], c, nm);
+    att_exp_half(xa[0], pa[0], pa[1], la);
   }
-  if (n_full < n_tiles) {
-    const int stage = n_full & 1, t0 = n_full * ATT_BK;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    // clear V^T entries of keys past the end (inside the caller's rows)
-    bf16 *vt = reinterpret_cast<bf16 *>(lds + stage * STAGE + KBYTES);
-    const int valid = sk - t0;
-    for (int x = tid; x < HD * ATT_BK; x += NT) {
-      const int row = x / ATT_BK, key = x % ATT_BK;
-      if (key >= valid) {
-        const int phys = (key >> 3) ^ ((row >> 1) & 7);
-        vt[row * ATT_BK + phys * 8 + (key & 7)] = (bf16)0.0f;
-      }
-    }
-    __syncthreads();
-    tile(std::true_type{}, stage, t0);
+
+  // ---- steps: pairs with full next tiles (stage parity known), then the
+  // odd one, the step whose next tile is ragged, and the last tile
+  const int n_plain = (ragged && n_tiles > 1) ? n_tiles - 2 : n_tiles - 1;
+  int i = 0;
+  for (; i + 1 < n_plain; i += 2) {
+    step(std::true_type{}, std::false_type{}, xa, pa, la, xb, pb, lb, i, 0);
+    step(std::true_type{}, std::false_type{}, xb, pb, lb, xa, pa, la, i + 1, 1);
   }
+  auto take_b = [&]() {
+    xa[0] = xb[0]; xa[1] = xb[1];
+    pa[0] = pb[0]; pa[1] = pb[1];
+    la = lb;
+  };
+  if (i < n_plain) {
+    step(std::true_type{}, std::false_type{}, xa, pa, la, xb, pb, lb, i, 0);
+    ++i;
+    take_b();
+  }
+  if (ragged && n_tiles > 1) {
+    step(std::true_type{}, std::true_type{}, xa, pa, la, xb, pb, lb, i, i & 1);
+    ++i;
+    take_b();
+  }
+  step(std::false_type{}, std::false_type{}, xa, pa, la, xb, pb, lb, i, i & 1);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
@@ -494,7 +625,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_bf16_kernel(AttnArgs p) 
       for (int j = 0; j < 4; ++j) {
         bf16x4 v4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v4[i] = (bf16)(o[t][j * 4 + i] * inv);
+        for (int i2 = 0; i2 < 4; ++i2) v4[i2] = (bf16)(o[t][j * 4 + i2] * inv);
         *reinterpret_cast<bf16x4 *>(O + t * 32 + j * 8 + half * 4) = v4;
       }
   }
