@@ -51,6 +51,25 @@ __device__ __forceinline__ void mma32(const f32x8 &a, const f32x8 &b, f32x16 &c)
 // 16-byte global/LDS vector moves.
 struct alignas(16) U128 { uint32_t w[4]; };
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Words of a raw buffer resource over `bytes` bytes at `base` (no stride;
+// loads at offsets past the end return zero).
+__device__ __forceinline__ i32x4 buffer_words(const void *base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xFFFF), (int)bytes, 0x00020000};
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes lds_addr + 16 i (lds_addr is wave-uniform).  Issued as inline asm so
+// that the compiler does not make every later LDS read wait for all such
+// transfers in flight; callers order them with explicit vmcnt waits and
+// barriers.
+__device__ __forceinline__ void dma_to_lds16(i32x4 rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // GELU, tanh form: z/2 (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3),

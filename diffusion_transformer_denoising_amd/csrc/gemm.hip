@@ -49,14 +49,6 @@ __device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_bit_cast(U128, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// 16 bytes per lane from a buffer straight into LDS: lane i of the wave
-// writes lds_block + 16 i (lds_block is wave-uniform).
-__device__ __forceinline__ void gemm_lds_load16(__amdgpu_buffer_rsrc_t r, void *lds_block,
-                                                uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_block, 16,
-                                           voff, 0, 0, 0);
-}
-
 constexpr uint32_t OOB = 0x80000000u;  // an offset past every operand (sizes < 2^31 bytes)
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"
@@ -405,13 +397,14 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
   static_assert(4 * gemm_strip_floats<bf16, WN>() * 4 <= NS * STAGE, "epilogue strips");
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, half = lane >> 5;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int M = p.M, N = p.N, K = p.K;
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(p.A, (uint32_t)((int64_t)M * p.lda * 2));
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.W, (uint32_t)((int64_t)N * p.ldw * 2));
+  const i32x4 ars = buffer_words(p.A, (uint32_t)((int64_t)M * p.lda * 2));
+  const i32x4 wrs = buffer_words(p.W, (uint32_t)((int64_t)N * p.ldw * 2));
 
   // Load instruction j of this wave fills stage rows j*32 + wave*8 .. +7; lane
   // i moves physical chunk i & 7 of row j*32 + wave*8 + (i >> 3).
@@ -427,10 +420,10 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   auto issue = [&](int kt, int stage) {
     const int k0 = kt * BK;
     const bool kin = k0 + logical * 8 < K;
-    char *sb = lds + stage * STAGE + wave * 1024;
+    const uint32_t sb = (uint32_t)(uintptr_t)lds + stage * STAGE + wave * 1024;
 #pragma unroll
     for (int j = 0; j < IPS; ++j)
-      gemm_lds_load16(j * 32 < BM ? ars : wrs, sb + j * 4096, kin ? src[j] + k0 * 2 : OOB);
+      dma_to_lds16(j * 32 < BM ? ars : wrs, sb + j * 4096, kin ? src[j] + k0 * 2 : OOB);
   };
 
   f32x16 acc[TM][TN];
@@ -443,36 +436,68 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
 
   const int swz = (l32 >> 1) & 7;
   const int arow = (wm * WM + l32) * ROWB, wrow = (BM + wn * WN + l32) * ROWB;
-  F af[2][TM], wf[2][TN];
-  auto lload = [&](const char *sb, int ch, int slot) {
-    const int off = ((ch * 2 + half) ^ swz) * 16;
-#pragma unroll
-    for (int a = 0; a < TM; ++a) af[slot][a] = *reinterpret_cast<const F *>(sb + arow + a * 32 * ROWB + off);
-#pragma unroll
-    for (int b = 0; b < TN; ++b) wf[slot][b] = *reinterpret_cast<const F *>(sb + wrow + b * 32 * ROWB + off);
-  };
-
-  const int KT = (K + BK - 1) / BK;
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s, s);
-  int stage = 0;
-  for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPS));  // slice kt landed (this wave)
-    __syncthreads();                                          // ... and for every wave
-    const int fill = stage == 0 ? NS - 1 : stage - 1;         // the stage read last step
-    issue(kt + NS - 1, fill);
+  // Fragments of a whole slice (4 k-chunks), double-buffered in registers:
+  // the next slice's fragments are read while this slice's MFMAs run, so the
+  // LDS latency is paid once per slice, under the products.
+  F af[2][4][TM], wf[2][4][TN];
+  auto lload = [&](int stage, int buf) {
     const char *sb = lds + stage * STAGE;
-    lload(sb, 0, 0);
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch) {
-      if (ch < 3) lload(sb, ch + 1, (ch + 1) & 1);
+      const int off = ((ch * 2 + half) ^ swz) * 16;
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+        af[buf][ch][a] = *reinterpret_cast<const F *>(sb + arow + a * 32 * ROWB + off);
+#pragma unroll
+      for (int b = 0; b < TN; ++b)
+        wf[buf][ch][b] = *reinterpret_cast<const F *>(sb + wrow + b * 32 * ROWB + off);
+    }
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) mma32(af[ch & 1][a], wf[ch & 1][b], acc[a][b]);
-    }
-    stage = stage + 1 == NS ? 0 : stage + 1;
+        for (int b = 0; b < TN; ++b) mma32(af[buf][ch][a], wf[buf][ch][b], acc[a][b]);
+  };
+
+  // Slices 0 .. NS-2 in flight; slice kt+1's fragments are read during step kt.
+  const int KT = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s) issue(s, s);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPS));  // slice 0 landed (this wave)
+  __syncthreads();
+  lload(0, 0);
+  // One step: slice kt+1 landed for every wave, slice kt+NS-1 into the stage
+  // of slice kt-1 (its fragments were read during step kt-2), fragments of
+  // slice kt+1 into register buffer nb, MFMAs of slice kt from buffer cb.
+  auto step = [&](int kt, int nstage, int fstage, int cb, int nb) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 3) * IPS));
+    __syncthreads();
+    issue(kt + NS - 1, fstage);
+    lload(nstage, nb);
+    mfmas(cb);
+    constexpr int NRD = 4 * (TM + TN), NMF = 4 * TM * TN;
+    constexpr int RPM = NRD / NMF > 0 ? NRD / NMF : 1;
+    static_for<NMF>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+    });
+  };
+  // stage of slice s is s % NS; tracked incrementally
+  int st1 = 1 % NS;            // stage of slice kt+1
+  int stf = NS - 1;            // stage of slice kt+NS-1
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    step(kt, st1, stf, 0, 1);
+    st1 = st1 + 1 == NS ? 0 : st1 + 1;
+    stf = stf + 1 == NS ? 0 : stf + 1;
+    step(kt + 1, st1, stf, 1, 0);
+    st1 = st1 + 1 == NS ? 0 : st1 + 1;
+    stf = stf + 1 == NS ? 0 : stf + 1;
   }
+  if (kt < KT) mfmas(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still be landing in LDS
   __syncthreads();
   gemm_epilogue<bf16, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(lds), m0, n0);
