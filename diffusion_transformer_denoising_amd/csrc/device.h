@@ -53,11 +53,18 @@ struct alignas(16) U128 { uint32_t w[4]; };
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left open).
+constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
+
 // Words of a raw buffer resource over `bytes` bytes at `base` (no stride;
 // loads at offsets past the end return zero).
 __device__ __forceinline__ i32x4 buffer_words(const void *base, uint32_t bytes) {
+  // wave-uniform by construction; readfirstlane keeps the words in SGPRs
   const uint64_t b = (uint64_t)base;
-  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xFFFF), (int)bytes, 0x00020000};
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+               __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xFFFF)),
+               __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane i of the wave

@@ -51,10 +51,6 @@ __device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 constexpr uint32_t OOB = 0x80000000u;  // an offset past every operand (sizes < 2^31 bytes)
 
-// s_waitcnt immediate for "at most n vector-memory operations outstanding"
-// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left open).
-constexpr int vmcnt_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | 0x0F70; }
-
 // Order this wave's LDS writes before its later LDS reads (other lanes' data).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -453,13 +449,28 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
         wf[buf][ch][b] = *reinterpret_cast<const F *>(sb + wrow + b * 32 * ROWB + off);
     }
   };
+  // With a single 32x32 tile per wave (64x64), odd k-chunks accumulate into a
+  // second set so consecutive MFMAs do not wait on each other's result.
+  constexpr bool DUAL = TM * TN == 1;
+  f32x16 acc2[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc2[a][b][e] = 0.0f;
   auto mfmas = [&](int buf) {
 #pragma unroll
     for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
       for (int a = 0; a < TM; ++a)
 #pragma unroll
-        for (int b = 0; b < TN; ++b) mma32(af[buf][ch][a], wf[buf][ch][b], acc[a][b]);
+        for (int b = 0; b < TN; ++b) {
+          if (DUAL && (ch & 1))
+            mma32(af[buf][ch][a], wf[buf][ch][b], acc2[a][b]);
+          else
+            mma32(af[buf][ch][a], wf[buf][ch][b], acc[a][b]);
+        }
   };
 
   // Slices 0 .. NS-2 in flight; slice kt+1's fragments are read during step kt.
@@ -498,6 +509,12 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
     stf = stf + 1 == NS ? 0 : stf + 1;
   }
   if (kt < KT) mfmas(0);
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) acc[a][b] += acc2[a][b];
+  }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still be landing in LDS
   __syncthreads();
   gemm_epilogue<bf16, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(lds), m0, n0);
