@@ -1,7 +1,7 @@
 """Benchmark: denoise steps per second of one DiT denoising step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--calibrate-copy]
 
 A step is one call of dit_denoise_step: time embedding, context projection,
 patch embedding, every DiT block (LayerNorm+adaLN, QKV projection, RoPE,
@@ -16,7 +16,10 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
   roofline       the kernel kind with the largest share of step time: its
                  algorithmic FLOPs (or bytes) per launch over its average launch
                  duration, from HIP events recorded around every launch during a
-                 second pass over the same K steps, against the MI355X peak
+                 second pass over the same K steps (less the time of an empty
+                 event pair on the same stream), against the MI355X peak;
+                 traffic = HBM bytes per launch from committed rocprofv3
+                 FETCH_SIZE / WRITE_SIZE runs (profiles/traffic.json), or null
   attention / gemm   TFLOP/s and fraction of the bf16 MFMA peak, same events
   cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
 """
@@ -130,6 +133,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (the known-size kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -139,6 +145,15 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+    if args.calibrate_copy:
+        n = 1 << 28  # float32 elements: 1 GiB read + 1 GiB written per copy
+        a = torch.ones(n, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 5}))
+        return 0
     from diffusion_transformer_denoising_amd import binding as B
     from diffusion_transformer_denoising_amd.model import DeviceDiT, torch_dtype
     from synth import params as SP
@@ -207,10 +222,22 @@ def main(argv=None) -> int:
     peak = PEAK_TFLOPS[cfg.dtype]
     att_tf, gemm_tf = group_rate(ATTN_KINDS), group_rate(GEMM_KINDS)
 
+    # An event pair recorded around a launch also times the two markers; an
+    # empty pair on the same stream measures that overhead, which is taken off
+    # the bracketed average of the roofline kernel.
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(200)]
+    for a0, a1 in pairs:
+        a0.record(stream)
+        a1.record(stream)
+    torch.cuda.synchronize()
+    overhead_ms = float(np.median([a0.elapsed_time(a1) for a0, a1 in pairs]))
+
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     unit, amount = work[dom]
     n_dom, ms_dom = prof[dom]
-    avg = ms_dom / n_dom / 1e3
+    avg_raw = ms_dom / n_dom / 1e3
+    avg = max(avg_raw - overhead_ms / 1e3, 0.5 * avg_raw)
     src = "attention.hip" if dom.startswith("attention") else (
         "gemm.hip" if dom.startswith("gemm") else "pointwise.hip")
     if unit == "flop":
@@ -223,7 +250,8 @@ def main(argv=None) -> int:
     roof["traffic"] = measured_traffic(dom, cfg.name)
     roof["kernel"] = dom
     roof["per_launch"] = {"work": amount, "work_unit": "FLOP" if unit == "flop" else "byte",
-                          "avg_us": round(avg * 1e6, 3), "source": src}
+                          "avg_us": round(avg * 1e6, 3), "avg_us_bracketed": round(avg_raw * 1e6, 3),
+                          "event_pair_overhead_us": round(overhead_ms * 1e3, 3), "source": src}
 
     fl = cfg.flops_per_step()
     out = {
