@@ -12,7 +12,7 @@ from synth.configs import get_config
 
 
 def require_gpu():
-    assert torch.cuda.is_available(), "GPU tests need an MI355X; run them with -m gpu on the GPU box"
+    assert torch.cuda.is_available(), "GPU tests need an MI355X (run them with -m gpu)"
 
 
 def announce(*what):
