@@ -223,6 +223,25 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, f32x16 (&acc)[B
   }
 }
 
+// Tile of this workgroup.  The grid is 1-D; workgroups are dispatched to the
+// 8 XCDs round-robin (id % 8), so id is first mapped to a contiguous range of
+// tiles per XCD, and that range is walked in groups of GM tile rows (row
+// fastest inside a group).  The ~32 workgroups an XCD runs at once then cover
+// a compact block of the output and share their A and W slices in that XCD's
+// L2 instead of spreading over all of them.
+__device__ __forceinline__ void gemm_tile_of(int nx, int ny, int &tm, int &tn) {
+  constexpr int GM = 4;
+  const int T = nx * ny;
+  const int id = blockIdx.x;
+  const int xcd = id & 7, local = id >> 3;
+  const int t = xcd * (T >> 3) + (xcd < (T & 7) ? xcd : (T & 7)) + local;
+  const int gsz = GM * nx;                       // tiles per group of GM rows
+  const int g = t / gsz, r = t - g * gsz;
+  const int rows = ny - g * GM < GM ? ny - g * GM : GM;  // rows in this (last) group
+  tm = g * GM + r % rows;
+  tn = r / rows;
+}
+
 // ---------------------------------------------------------------------------
 // Register-staged main loop (256x256 bf16; 64x64 fp32).
 // ---------------------------------------------------------------------------
@@ -245,9 +264,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
   const int M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  gemm_tile_of((N + BN - 1) / BN, (M + BM - 1) / BM, tm, tn);
+  const int m0 = tm * BM;
+  const int n0 = tn * BN;
 
   // Each thread moves the 16-byte piece kk of rows (tid >> 3) + 32 i.
   const int kk = (tid & 7) * VEC;
@@ -397,8 +418,10 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, half = lane >> 5;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int M = p.M, N = p.N, K = p.K;
+  // small grids are resident all at once: plain row-major tile order
+  const int nx = (N + BN - 1) / BN;
+  const int m0 = (blockIdx.x / nx) * BM, n0 = (blockIdx.x % nx) * BN;
   const i32x4 ars = buffer_words(p.A, (uint32_t)((int64_t)M * p.lda * 2));
   const i32x4 wrs = buffer_words(p.W, (uint32_t)((int64_t)N * p.ldw * 2));
 
@@ -522,7 +545,7 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
 
 template <typename T, int BM, int BN>
 static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+  dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM));
   switch (epi) {
     case EPI_STORE: gemm_kernel<T, BM, BN, EPI_STORE><<<grid, 256, 0, s>>>(a); break;
     case EPI_GELU: gemm_kernel<T, BM, BN, EPI_GELU><<<grid, 256, 0, s>>>(a); break;
@@ -536,7 +559,7 @@ static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
 
 template <int BM, int BN, int NS>
 static hipError_t launch_dl(Epilogue epi, const GemmArgs &a, hipStream_t s) {
-  dim3 grid((a.N + BN - 1) / BN, (a.M + BM - 1) / BM);
+  dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM));
   switch (epi) {
     case EPI_STORE: gemm_dl_kernel<BM, BN, NS, EPI_STORE><<<grid, 256, 0, s>>>(a); break;
     case EPI_GELU: gemm_dl_kernel<BM, BN, NS, EPI_GELU><<<grid, 256, 0, s>>>(a); break;
