@@ -90,10 +90,25 @@ __device__ __forceinline__ float gelu_tanh(float z) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + fast_exp2(-1.4426950408889634f * z)); }
 
+// Sum over the 64 lanes of a wave, in every lane.  Butterflies inside each row
+// of 16 lanes use DPP lane moves (no LDS round trip): xor 1, xor 2, then the
+// half-row and row mirrors, which pair equal-valued groups of 4 and 8; the four
+// row sums are then read out as scalars.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x141>(v);  // row_half_mirror: quads 0 <-> 1 of each 8
+  v += dpp_mov<0x140>(v);  // row_mirror: halves 0 <-> 1 of each 16
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 // Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(<N-1>).

@@ -8,13 +8,15 @@ namespace dit {
 
 // ---------------------------------------------------------------------------
 // LayerNorm + modulation.  One wave per row: the row is held in registers
-// (float4 per lane per 256 columns), mean and variance are two wave
-// reductions over the held values, then y = (x - mu) * rstd * (1 + scale) +
-// shift is written in the element type.  Rows up to 20 * 256 = 5120 wide.
+// (NV float4 per lane, NV = ceil(D / 256), fixed per instantiation so the
+// loads are issued together without per-chunk branches), mean and variance
+// are two wave reductions over the held values (two-pass), then
+// y = (x - mu) * rstd * (1 + scale) + shift is written in the element type.
+// Rows up to 20 * 256 = 5120 wide.
 // ---------------------------------------------------------------------------
 constexpr int LN_MAXV = 20;
 
-template <typename T>
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x, int rows, int D,
                                                      float eps, const float *__restrict__ shift,
                                                      const float *__restrict__ scale,
@@ -24,20 +26,18 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x
   if (row >= rows) return;
   const float *xr = x + (int64_t)row * D;
   const int nv = D >> 2;  // float4 count
-  f32x4 v[LN_MAXV];
+  f32x4 v[NV];
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c = lane + i * 64;
-    if (c < nv) {
-      v[i] = *reinterpret_cast<const f32x4 *>(xr + 4 * c);
-      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
-    }
+    v[i] = c < nv ? *reinterpret_cast<const f32x4 *>(xr + 4 * c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
   }
   const float mu = wave_sum(s) / (float)D;
   float q = 0.0f;
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c = lane + i * 64;
     if (c < nv) {
 #pragma unroll
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x
   const float rstd = 1.0f / sqrtf(var + eps);
   T *yr = y + (int64_t)row * D;
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int c = lane + i * 64;
     if (c < nv) {
       f32x4 o;
@@ -75,15 +75,27 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x
   }
 }
 
+// launch the instantiation with NV == nvl (NV = 1 .. LN_MAXV)
+template <typename T, int NV = 1>
+static void launch_ln_t(int nvl, dim3 grid, hipStream_t s, const float *x, int rows, int D, float eps,
+                        const float *shift, const float *scale, T *y) {
+  if (nvl == NV) {
+    ln_mod_kernel<T, NV><<<grid, 256, 0, s>>>(x, rows, D, eps, shift, scale, y);
+  } else if constexpr (NV < LN_MAXV) {
+    launch_ln_t<T, NV + 1>(nvl, grid, s, x, rows, D, eps, shift, scale, y);
+  }
+}
+
 hipError_t launch_ln_modulate(DType dt, const float *x, int rows, int D, float eps,
                               const float *shift, const float *scale, void *y, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (D % 4 != 0 || D > LN_MAXV * 256) return hipErrorInvalidValue;
   dim3 grid((rows + 3) / 4);
+  const int nvl = (D / 4 + 63) / 64;
   if (dt == DT_BF16)
-    ln_mod_kernel<bf16><<<grid, 256, 0, s>>>(x, rows, D, eps, shift, scale, static_cast<bf16 *>(y));
+    launch_ln_t<bf16>(nvl, grid, s, x, rows, D, eps, shift, scale, static_cast<bf16 *>(y));
   else
-    ln_mod_kernel<float><<<grid, 256, 0, s>>>(x, rows, D, eps, shift, scale, static_cast<float *>(y));
+    launch_ln_t<float>(nvl, grid, s, x, rows, D, eps, shift, scale, static_cast<float *>(y));
   return hipGetLastError();
 }
 
