@@ -62,7 +62,8 @@ def kind_work(cfg) -> dict:
         "gemm_qkv_rope": ("flop", 2 * S * D * 3 * D),
         "gemm_o": ("flop", 2 * S * D * D),
         "gemm_cross_q": ("flop", 2 * S * D * D),
-        "gemm_cross_kv": ("flop", 2 * L * D * 2 * D),
+        # one grouped launch per step computes every block's cross K / V^T
+        "gemm_cross_kv": ("flop", cfg.num_blocks * 2 * L * D * 2 * D),
         "gemm_cross_o": ("flop", 2 * S * D * D),
         "gemm_mlp1_gelu": ("flop", 2 * S * D * F),
         "gemm_mlp2": ("flop", 2 * S * F * D),

@@ -30,8 +30,10 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct Plan {
   int64_t S, S_pad, L_pad, P, D, F, H, d;
   size_t es;  // element size
+  // kc, vct hold the cross K / V^T of every block: [B][L_max][D], [B][D][L_pad];
+  // gtab is the device table {ckv_w[0..B), ckv_b[0..B)} of the grouped projection
   size_t cos_t, sin_t, x, y, q, k, vt, o, h, c, kc, vct, patches, u, sinus, h1, temb, e, bmod,
-      hmod;
+      hmod, gtab;
   size_t total;
 };
 
@@ -62,8 +64,8 @@ bool plan_layout(const dit_config &c, Plan &p) {
   p.o = take(es * p.S * p.D);
   p.h = take(es * p.S * p.F);
   p.c = take(es * (size_t)c.ctx_len_max * p.D);
-  p.kc = take(es * (size_t)c.ctx_len_max * p.D);
-  p.vct = take(es * p.D * p.L_pad);
+  p.kc = take(es * (size_t)c.num_blocks * c.ctx_len_max * p.D);
+  p.vct = take(es * (size_t)c.num_blocks * p.D * p.L_pad);
   p.patches = take(es * p.S * p.P);
   p.u = take(f4 * p.S * p.P);
   p.sinus = take(f4 * c.freq_dim);
@@ -72,6 +74,7 @@ bool plan_layout(const dit_config &c, Plan &p) {
   p.e = take(f4 * 6 * p.D);
   p.bmod = take(f4 * 6 * p.D * c.num_blocks);
   p.hmod = take(f4 * 2 * p.D);
+  p.gtab = take(sizeof(void *) * 2 * (size_t)c.num_blocks);
   p.total = off;
   return true;
 }
@@ -215,14 +218,16 @@ GemmArgs gemm(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int
 
 // One block on the residual stream x [S, D] with projected context ctx [L, D].
 dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, const float *mod,
-                     hipStream_t s) {
+                     hipStream_t s, bool ckv_ready) {
   const dit_config &c = m->cfg;
   const Plan &p = m->plan;
   const dit_block_weights &w = m->blocks[b];
   const int S = (int)p.S, D = (int)p.D, F = (int)p.F;
   void *y = m->buf<void>(p.y), *q = m->buf<void>(p.q), *k = m->buf<void>(p.k);
   void *vt = m->buf<void>(p.vt), *o = m->buf<void>(p.o), *h = m->buf<void>(p.h);
-  void *kc = m->buf<void>(p.kc), *vct = m->buf<void>(p.vct);
+  // this block's cross K / V^T slots
+  void *kc = m->buf<char>(p.kc) + p.es * (size_t)b * c.ctx_len_max * p.D;
+  void *vct = m->buf<char>(p.vct) + p.es * (size_t)b * p.D * p.L_pad;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
 
   // self-attention branch: y = LN(x)(1 + scale_a) + shift_a
@@ -255,7 +260,7 @@ dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, cons
     a.out = q; a.ldo = D;
     DIT_RUN(m, PK_GEMM_CQ, s, launch_gemm(m->dt, EPI_STORE, a, s));
   }
-  {
+  if (!ckv_ready) {
     GemmArgs a = gemm(ctx, D, w.ckv_w, D, L, 2 * D, D, w.ckv_b);
     a.seg_width = D;
     a.seg_ptr[0] = kc; a.seg_ld[0] = D; a.seg_trans[0] = 0;
@@ -342,7 +347,17 @@ dit_status dit_create(const dit_config *cfg, const dit_weights *weights, void *w
   m->ws = static_cast<char *>(workspace);
   m->plan = p;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_rope_tables(m->buf<float>(p.cos_t), m->buf<float>(p.sin_t),
+  // device table of the per-block cross K/V weights and biases (grouped launch)
+  std::vector<const void *> tab(2 * (size_t)cfg->num_blocks);
+  for (int b = 0; b < cfg->num_blocks; ++b) {
+    tab[b] = weights->blocks[b].ckv_w;
+    tab[cfg->num_blocks + b] = weights->blocks[b].ckv_b;
+  }
+  hipError_t e = hipMemcpyAsync(m->ws + p.gtab, tab.data(), tab.size() * sizeof(void *),
+                                hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // `tab` is released on return
+  if (e == hipSuccess)
+    e = launch_rope_tables(m->buf<float>(p.cos_t), m->buf<float>(p.sin_t),
                                     cfg->lat_f / cfg->patch_f, cfg->lat_h / cfg->patch_h,
                                     cfg->lat_w / cfg->patch_w, cfg->head_dim, cfg->rope_f,
                                     cfg->rope_h, cfg->rope_w, cfg->rope_theta, s);
@@ -364,7 +379,7 @@ dit_status dit_block_forward(dit_model *m, int32_t block, float *x, const void *
   if (!m || !ok_ptr(x) || !ok_ptr(ctx) || !ok_ptr(mod)) return DIT_ERR_INVALID_ARG;
   if (block < 0 || block >= m->cfg.num_blocks) return DIT_ERR_SHAPE;
   if (ctx_len < 1 || ctx_len > m->cfg.ctx_len_max) return DIT_ERR_SHAPE;
-  return run_block(m, block, x, ctx, ctx_len, mod, static_cast<hipStream_t>(stream));
+  return run_block(m, block, x, ctx, ctx_len, mod, static_cast<hipStream_t>(stream), false);
 }
 
 dit_status dit_denoise_step(dit_model *m, float *X, const void *ctx, int32_t ctx_len, float t,
@@ -400,8 +415,22 @@ dit_status dit_denoise_step(dit_model *m, float *X, const void *ctx, int32_t ctx
     a.ldo = D;
     DIT_RUN(m, PK_GEMM_PE, s, launch_gemm(m->dt, EPI_STORE_F32, a, s));
   }
+  // cross K / V^T of every block in one grouped launch: they depend on the
+  // context only, not on the residual stream
+  {
+    GemmArgs a = gemm(cproj, D, nullptr, D, ctx_len, 2 * D, D, nullptr);
+    a.seg_width = D;
+    a.seg_ptr[0] = m->buf<void>(p.kc); a.seg_ld[0] = D; a.seg_trans[0] = 0;
+    a.seg_ptr[1] = m->buf<void>(p.vct); a.seg_ld[1] = p.L_pad; a.seg_trans[1] = 1;
+    a.groups = c.num_blocks;
+    a.gw = m->buf<const void *>(p.gtab);
+    a.gbias = m->buf<const void *>(p.gtab) + c.num_blocks;
+    a.seg_gstride[0] = (int64_t)c.ctx_len_max * D;
+    a.seg_gstride[1] = (int64_t)D * p.L_pad;
+    DIT_RUN(m, PK_GEMM_CKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
+  }
   for (int b = 0; b < c.num_blocks; ++b) {
-    st = run_block(m, b, x, cproj, ctx_len, bmod + (int64_t)b * 6 * D, s);
+    st = run_block(m, b, x, cproj, ctx_len, bmod + (int64_t)b * 6 * D, s, true);
     if (st != DIT_OK) return st;
   }
   DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, hmod, hmod + D, m->buf<void>(p.y), s));

@@ -78,7 +78,8 @@ constexpr int gemm_strip_floats() {
 
 template <typename T, int BM, int BN, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, f32x16 (&acc)[BM / 64][BN / 64],
-                                              float *scratch, int m0, int n0) {
+                                              float *scratch, int m0, int n0, const void *bias_g,
+                                              int g) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   constexpr int SROW = WN + 4;                        // fp32 strip row stride
   constexpr int TROW = 32 + 16 / (int)sizeof(T);      // transposed strip row stride
@@ -88,7 +89,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, f32x16 (&acc)[B
   const int M = p.M, N = p.N;
   float *strip = scratch + wave * REG;
   T *stripT = reinterpret_cast<T *>(strip);
-  const T *bias = static_cast<const T *>(p.bias);
+  const T *bias = static_cast<const T *>(bias_g);
   const int colbase = n0 + wn * WN;
   int segc = colbase, trans = 0, rope = 0;
   void *dst = p.out;
@@ -98,7 +99,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, f32x16 (&acc)[B
     segc = colbase - seg * p.seg_width;
     trans = p.seg_trans[seg];
     rope = p.seg_rope[seg];
-    dst = p.seg_ptr[seg];
+    dst = static_cast<T *>(p.seg_ptr[seg]) + (int64_t)g * p.seg_gstride[seg];
     ld = p.seg_ld[seg];
   }
   constexpr int VE = EPI == EPI_RESIDUAL || EPI == EPI_STORE_F32 || sizeof(T) == 4 ? 4 : 8;
@@ -223,7 +224,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, f32x16 (&acc)[B
   }
 }
 
-// Tile of this workgroup.  The grid is 1-D; workgroups are dispatched to the
+// Tile of this workgroup.  grid.x is 1-D over tiles; workgroups are dispatched to the
 // 8 XCDs round-robin (id % 8), so id is first mapped to a contiguous range of
 // tiles per XCD, and that range is walked in groups of GM tile rows (row
 // fastest inside a group).  The ~32 workgroups an XCD runs at once then cover
@@ -240,6 +241,19 @@ __device__ __forceinline__ void gemm_tile_of(int nx, int ny, int &tm, int &tn) {
   const int rows = ny - g * GM < GM ? ny - g * GM : GM;  // rows in this (last) group
   tm = g * GM + r % rows;
   tn = r / rows;
+}
+
+// W and bias of this workgroup's problem (grid.y selects the group).
+__device__ __forceinline__ void gemm_group(const GemmArgs &p, const void *&W, const void *&bias,
+                                           int &g) {
+  g = 0;
+  W = p.W;
+  bias = p.bias;
+  if (p.gw) {  // a table is given: it holds the weights, one group per grid row
+    g = blockIdx.y;
+    W = p.gw[g];
+    bias = p.gbias[g];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -274,7 +288,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const int kk = (tid & 7) * VEC;
   const int r0 = tid >> 3;
   const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(p.A, (uint32_t)((int64_t)M * p.lda * sizeof(T)));
-  const __amdgpu_buffer_rsrc_t rw_src = make_rsrc(p.W, (uint32_t)((int64_t)N * p.ldw * sizeof(T)));
+  const void *Wg, *bias_g;
+  int g;
+  gemm_group(p, Wg, bias_g, g);
+  const __amdgpu_buffer_rsrc_t rw_src = make_rsrc(Wg, (uint32_t)((int64_t)N * p.ldw * sizeof(T)));
   const uint32_t a_off0 = (uint32_t)(((int64_t)(m0 + r0) * p.lda + kk) * sizeof(T));
   const uint32_t w_off0 = (uint32_t)(((int64_t)(n0 + r0) * p.ldw + kk) * sizeof(T));
   const uint32_t a_step = (uint32_t)(32 * p.lda * sizeof(T));
@@ -393,7 +410,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 
 
   __syncthreads();  // every wave is done with the main-loop buffers
-  gemm_epilogue<T, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0);
+  gemm_epilogue<T, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0, bias_g, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -423,7 +440,10 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   const int nx = (N + BN - 1) / BN;
   const int m0 = (blockIdx.x / nx) * BM, n0 = (blockIdx.x % nx) * BN;
   const i32x4 ars = buffer_words(p.A, (uint32_t)((int64_t)M * p.lda * 2));
-  const i32x4 wrs = buffer_words(p.W, (uint32_t)((int64_t)N * p.ldw * 2));
+  const void *Wg, *bias_g;
+  int g;
+  gemm_group(p, Wg, bias_g, g);
+  const i32x4 wrs = buffer_words(Wg, (uint32_t)((int64_t)N * p.ldw * 2));
 
   // Load instruction j of this wave fills stage rows j*32 + wave*8 .. +7; lane
   // i moves physical chunk i & 7 of row j*32 + wave*8 + (i >> 3).
@@ -540,12 +560,12 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still be landing in LDS
   __syncthreads();
-  gemm_epilogue<bf16, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(lds), m0, n0);
+  gemm_epilogue<bf16, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(lds), m0, n0, bias_g, g);
 }
 
 template <typename T, int BM, int BN>
 static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
-  dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM));
+  dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM), a.gw ? a.groups : 1);
   switch (epi) {
     case EPI_STORE: gemm_kernel<T, BM, BN, EPI_STORE><<<grid, 256, 0, s>>>(a); break;
     case EPI_GELU: gemm_kernel<T, BM, BN, EPI_GELU><<<grid, 256, 0, s>>>(a); break;
@@ -559,7 +579,7 @@ static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
 
 template <int BM, int BN, int NS>
 static hipError_t launch_dl(Epilogue epi, const GemmArgs &a, hipStream_t s) {
-  dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM));
+  dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM), a.gw ? a.groups : 1);
   switch (epi) {
     case EPI_STORE: gemm_dl_kernel<BM, BN, NS, EPI_STORE><<<grid, 256, 0, s>>>(a); break;
     case EPI_GELU: gemm_dl_kernel<BM, BN, NS, EPI_GELU><<<grid, 256, 0, s>>>(a); break;
@@ -579,9 +599,10 @@ bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) 
 
 // Tile choice (measured on MI355X): 256x256 once the grid has at least half
 // a tile per CU, else 128x128 with at least one tile per CU, else 64x64.
-static int pick_tile(int M, int N) {
-  const int64_t t256 = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+static int pick_tile(int M, int N, int groups) {
+  const int64_t G = groups > 1 ? groups : 1;
+  const int64_t t256 = G * ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t t128 = G * ((M + 127) / 128) * ((N + 127) / 128);
   if (t256 >= 128) return 1;
   if (t128 >= 256) return 2;
   return 3;
@@ -589,9 +610,11 @@ static int pick_tile(int M, int N) {
 
 hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile) {
   if (a.M <= 0 || a.N <= 0 || a.K <= 0) return hipSuccess;
+  // weights come from W, or (grouped) from the tables, which then need >= 1 group
+  if (a.gw ? (!a.gbias || a.groups < 1) : (a.W == nullptr || a.groups > 1)) return hipErrorInvalidValue;
   if (!gemm_offsets_fit(dt, a.M, a.lda, a.N, a.ldw)) return hipErrorInvalidValue;
   if (dt == DT_BF16) {
-    if (tile == 0) tile = pick_tile(a.M, a.N);
+    if (tile == 0) tile = pick_tile(a.M, a.N, a.groups);
     // a split store needs every wave's column strip inside one segment
     while (epi == EPI_SPLIT && tile < 3 && a.seg_width % (tile == 1 ? 128 : 64) != 0) ++tile;
     switch (tile) {

@@ -39,6 +39,13 @@ struct GemmArgs {
   int seg_rope[3];    // rotate (2j, 2j+1) column pairs of this segment
   const float *rope_cos, *rope_sin;  // [M, rope_half_d] tables, per head
   int rope_half_d;
+  // Grouped launch: `groups` independent problems with the same A and shape;
+  // group g uses W = gw[g] and bias = gbias[g] (device tables) and writes split
+  // segment s at seg_ptr[s] + g * seg_gstride[s] elements.  groups <= 1: none.
+  int groups;
+  const void *const *gw;
+  const void *const *gbias;
+  int64_t seg_gstride[3];
 };
 // tile: 0 automatic, 1 256x256, 2 128x128, 3 64x64 (bf16); fp32 uses 64x64.
 hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile = 0);
