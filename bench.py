@@ -77,7 +77,8 @@ def kind_work(cfg) -> dict:
         "patchify": ("byte", n_lat * (4 + es)),
         # read velocity tokens, read-modify-write the latents
         "unpatchify_euler": ("byte", n_lat * 4 * 3),
-        "time_embedding": ("byte", es * (cfg.freq_dim * D + D * D + 6 * D * D)),
+        # three GEMV launches per step; the per-launch figure is their mean
+        "time_embedding": ("byte", es * (cfg.freq_dim * D + D * D + 6 * D * D) // 3),
     }
 
 

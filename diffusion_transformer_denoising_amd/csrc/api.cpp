@@ -31,9 +31,11 @@ struct Plan {
   int64_t S, S_pad, L_pad, P, D, F, H, d;
   size_t es;  // element size
   // kc, vct hold the cross K / V^T of every block: [B][L_max][D], [B][D][L_pad];
-  // gtab is the device table {ckv_w[0..B), ckv_b[0..B)} of the grouped projection
-  size_t cos_t, sin_t, x, y, q, k, vt, o, h, c, kc, vct, patches, u, sinus, h1, temb, e, bmod,
-      hmod, gtab;
+  // gtab is a device table of weight pointers: ckv_w[0..B), ckv_b[0..B) (the
+  // grouped cross K/V projection), table[0..B) (per-block modulation tables),
+  // then the two rows of the head table
+  size_t cos_t, sin_t, x, y, q, k, vt, o, h, c, kc, vct, patches, u, h1, temb, e, bmod, hmod,
+      gtab;
   size_t total;
 };
 
@@ -68,13 +70,12 @@ bool plan_layout(const dit_config &c, Plan &p) {
   p.vct = take(es * (size_t)c.num_blocks * p.D * p.L_pad);
   p.patches = take(es * p.S * p.P);
   p.u = take(f4 * p.S * p.P);
-  p.sinus = take(f4 * c.freq_dim);
   p.h1 = take(f4 * p.D);
   p.temb = take(f4 * p.D);
   p.e = take(f4 * 6 * p.D);
   p.bmod = take(f4 * 6 * p.D * c.num_blocks);
   p.hmod = take(f4 * 2 * p.D);
-  p.gtab = take(sizeof(void *) * 2 * (size_t)c.num_blocks);
+  p.gtab = take(sizeof(void *) * (3 * (size_t)c.num_blocks + 2));
   p.total = off;
   return true;
 }
@@ -296,15 +297,18 @@ dit_status run_time_path(dit_model *m, float t, float *bmod, float *hmod, float 
   const dit_config &c = m->cfg;
   const Plan &p = m->plan;
   const int D = (int)p.D;
-  float *sinus = m->buf<float>(p.sinus), *h1 = m->buf<float>(p.h1), *e = m->buf<float>(p.e);
-  DIT_RUN(m, PK_TIME, s, launch_sinusoid(t, c.freq_dim, sinus, s));
-  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.t1_w, m->g.t1_b, sinus, h1, D, c.freq_dim, false, s));
-  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.t2_w, m->g.t2_b, h1, temb, D, D, true, s));
-  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.mod_w, m->g.mod_b, temb, e, 6 * D, D, true, s));
-  std::vector<const void *> tables(c.num_blocks);
-  for (int b = 0; b < c.num_blocks; ++b) tables[b] = m->blocks[b].table;
-  DIT_RUN(m, PK_TIME, s, launch_block_mods(m->dt, e, tables.data(), c.num_blocks, bmod, D, s));
-  DIT_RUN(m, PK_TIME, s, launch_head_mod(m->dt, m->g.head_table, temb, hmod, D, s));
+  float *h1 = m->buf<float>(p.h1), *e = m->buf<float>(p.e);
+  const void *const *tab = m->buf<const void *>(p.gtab);
+  const int B = c.num_blocks;
+  // h1 = W1 sinusoid(t) + b1 (sinusoid formed inside the launch)
+  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.t1_w, m->g.t1_b, nullptr, t, h1, D, c.freq_dim,
+                                     false, nullptr, 0, nullptr, s));
+  // temb = W2 SiLU(h1) + b2; head modulation = head table rows + temb
+  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.t2_w, m->g.t2_b, h1, 0.0f, temb, D, D, true,
+                                     tab + 3 * B, 2, hmod, s));
+  // e = Wm SiLU(temb) + bm; block b modulation = table_b + e
+  DIT_RUN(m, PK_TIME, s, launch_gemv(m->dt, m->g.mod_w, m->g.mod_b, temb, 0.0f, e, 6 * D, D, true,
+                                     tab + 2 * B, B, bmod, s));
   return DIT_OK;
 }
 
@@ -348,11 +352,16 @@ dit_status dit_create(const dit_config *cfg, const dit_weights *weights, void *w
   m->plan = p;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // device table of the per-block cross K/V weights and biases (grouped launch)
-  std::vector<const void *> tab(2 * (size_t)cfg->num_blocks);
-  for (int b = 0; b < cfg->num_blocks; ++b) {
+  const int B = cfg->num_blocks;
+  std::vector<const void *> tab(3 * (size_t)B + 2);
+  for (int b = 0; b < B; ++b) {
     tab[b] = weights->blocks[b].ckv_w;
-    tab[cfg->num_blocks + b] = weights->blocks[b].ckv_b;
+    tab[B + b] = weights->blocks[b].ckv_b;
+    tab[2 * B + b] = weights->blocks[b].table;
   }
+  const size_t es = cfg->dtype == DIT_BF16 ? 2 : 4;
+  tab[3 * B] = weights->global.head_table;
+  tab[3 * B + 1] = static_cast<const char *>(weights->global.head_table) + es * cfg->hidden;
   hipError_t e = hipMemcpyAsync(m->ws + p.gtab, tab.data(), tab.size() * sizeof(void *),
                                 hipMemcpyHostToDevice, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);  // `tab` is released on return

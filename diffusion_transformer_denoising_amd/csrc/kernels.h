@@ -88,20 +88,12 @@ hipError_t launch_unpatchify_euler(const float *u, float *X, float *v_out, float
 // X[i] += dt * v[i], i < n.
 hipError_t launch_euler(float *X, const float *v, int64_t n, float dt, hipStream_t s);
 
-// Timestep sinusoid: out[j] = cos(t w_j), out[half + j] = sin(t w_j), w_j = 10000^(-j/half).
-hipError_t launch_sinusoid(float t, int dim, float *out, hipStream_t s);
-
-// y[n] = sum_k W[n, k] * act(x[k]) + b[n]; act = SiLU when silu_in, else identity.
-hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, float *y, int N,
-                       int K, bool silu_in, hipStream_t s);
-
-// block_mod[b, :, :] = e + table_b for up to `count` blocks starting at `first`;
-// tables T [6, D].
-hipError_t launch_block_mods(DType dt, const float *e, const void *const *tables, int count,
-                             float *block_mod, int D, hipStream_t s);
-
-// head_mod[j, :] = head_table[j, :] + temb, j = 0, 1.
-hipError_t launch_head_mod(DType dt, const void *head_table, const float *temb, float *head_mod,
-                           int D, hipStream_t s);
+// y[n] = sum_k W[n, k] * in[k] + b[n], in = act(x) (act = SiLU when silu_in,
+// else identity) or, with x == NULL, the timestep sinusoid of width K:
+// [cos(t w_j), sin(t w_j)], w_j = 10000^(-j / (K/2)).  With nfan > 0 also
+// fan_out[f, n] = y[n] + fan[f][n], f < nfan, fan a device table of T [N] rows.
+hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, float t, float *y,
+                       int N, int K, bool silu_in, const void *const *fan, int nfan, float *fan_out,
+                       hipStream_t s);
 
 }  // namespace dit

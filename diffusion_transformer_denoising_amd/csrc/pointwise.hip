@@ -233,32 +233,33 @@ hipError_t launch_euler(float *X, const float *v, int64_t n, float dt, hipStream
 // ---------------------------------------------------------------------------
 // Time path.
 // ---------------------------------------------------------------------------
-__global__ void sinusoid_kernel(double t, int half, float *out) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= half) return;
-  const double a = t * pow(10000.0, -(double)j / (double)half);
-  out[j] = (float)cos(a);
-  out[half + j] = (float)sin(a);
-}
-
-hipError_t launch_sinusoid(float t, int dim, float *out, hipStream_t s) {
-  const int half = dim / 2;
-  sinusoid_kernel<<<(half + 127) / 128, 128, 0, s>>>((double)t, half, out);
-  return hipGetLastError();
-}
-
 // One wave per output: the wave walks the weight row in 16-byte pieces.  The
-// input vector (SiLU applied when asked) is staged once per workgroup in LDS.
+// input vector is staged once per workgroup in LDS: x (SiLU applied when
+// asked) or, with x == NULL, the timestep sinusoid of width K computed in
+// double: [cos(t w_j), sin(t w_j)], w_j = 10000^(-j / (K/2)).
+// Fan-out epilogue: with nfan > 0, fan_out[f * N + n] = y[n] + fan[f][n] for
+// every f < nfan (fan is a device table of T [N] rows), which builds the
+// per-block and head modulation vectors in the same launch.
 constexpr int GEMV_MAXK = 8192;
 
 template <typename T>
 __global__ __launch_bounds__(256) void gemv_kernel(const T *__restrict__ W, const T *__restrict__ b,
-                                                   const float *__restrict__ x,
+                                                   const float *__restrict__ x, double t,
                                                    float *__restrict__ y, int N, int K,
-                                                   int silu_in) {
+                                                   int silu_in, const void *const *__restrict__ fan,
+                                                   int nfan, float *__restrict__ fan_out) {
   constexpr int VEC = 16 / sizeof(T);
   __shared__ float xs[GEMV_MAXK];
-  for (int k = threadIdx.x; k < K; k += 256) xs[k] = silu_in ? silu(x[k]) : x[k];
+  if (x) {
+    for (int k = threadIdx.x; k < K; k += 256) xs[k] = silu_in ? silu(x[k]) : x[k];
+  } else {
+    const int half = K / 2;
+    for (int j = threadIdx.x; j < half; j += 256) {
+      const double a = t * pow(10000.0, -(double)j / (double)half);
+      xs[j] = (float)cos(a);
+      xs[half + j] = (float)sin(a);
+    }
+  }
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -271,75 +272,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T *__restrict__ W, cons
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc += to_f32(w[e]) * xs[k0 + e];
   }
-  acc = wave_sum(acc);
-  if (lane == 0) y[n] = acc + (b ? to_f32(b[n]) : 0.0f);
+  const float yv = wave_sum(acc) + (b ? to_f32(b[n]) : 0.0f);  // in every lane
+  if (lane == 0) y[n] = yv;
+  for (int f = lane; f < nfan; f += 64)
+    fan_out[(int64_t)f * N + n] = yv + to_f32(static_cast<const T *>(fan[f])[n]);
 }
 
-hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, float *y, int N,
-                       int K, bool silu_in, hipStream_t s) {
-  if (K > GEMV_MAXK) return hipErrorInvalidValue;
+hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, float t, float *y,
+                       int N, int K, bool silu_in, const void *const *fan, int nfan, float *fan_out,
+                       hipStream_t s) {
+  if (K > GEMV_MAXK || (!x && (K & 1)) || (nfan > 0 && (!fan || !fan_out))) return hipErrorInvalidValue;
   dim3 grid((N + 3) / 4);
   if (dt == DT_BF16)
-    gemv_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<const bf16 *>(W),
-                                           static_cast<const bf16 *>(b), x, y, N, K, silu_in);
+    gemv_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<const bf16 *>(W), static_cast<const bf16 *>(b),
+                                           x, (double)t, y, N, K, silu_in, fan, nfan, fan_out);
   else
-    gemv_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(W),
-                                            static_cast<const float *>(b), x, y, N, K, silu_in);
-  return hipGetLastError();
-}
-
-constexpr int MOD_MAX_BLOCKS = 64;
-struct TablePtrs { const void *p[MOD_MAX_BLOCKS]; };
-
-template <typename T>
-__global__ __launch_bounds__(256) void block_mods_kernel(const float *__restrict__ e,
-                                                         TablePtrs tabs, int count,
-                                                         float *__restrict__ out, int D) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t per = 6 * (int64_t)D;
-  if (idx >= per * count) return;
-  const int b = (int)(idx / per);
-  const int64_t r = idx - b * per;
-  out[idx] = e[r] + to_f32(static_cast<const T *>(tabs.p[b])[r]);
-}
-
-hipError_t launch_block_mods(DType dt, const float *e, const void *const *tables, int count,
-                             float *block_mod, int D, hipStream_t s) {
-  for (int first = 0; first < count; first += MOD_MAX_BLOCKS) {
-    const int n = count - first < MOD_MAX_BLOCKS ? count - first : MOD_MAX_BLOCKS;
-    TablePtrs tp;
-    for (int i = 0; i < n; ++i) tp.p[i] = tables[first + i];
-    const int64_t total = 6 * (int64_t)D * n;
-    dim3 grid((unsigned)((total + 255) / 256));
-    float *dst = block_mod + (int64_t)first * 6 * D;
-    if (dt == DT_BF16)
-      block_mods_kernel<bf16><<<grid, 256, 0, s>>>(e, tp, n, dst, D);
-    else
-      block_mods_kernel<float><<<grid, 256, 0, s>>>(e, tp, n, dst, D);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  return hipSuccess;
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void head_mod_kernel(const T *__restrict__ table,
-                                                       const float *__restrict__ temb,
-                                                       float *__restrict__ out, int D) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= 2 * D) return;
-  out[i] = to_f32(table[i]) + temb[i % D];
-}
-
-hipError_t launch_head_mod(DType dt, const void *head_table, const float *temb, float *head_mod,
-                           int D, hipStream_t s) {
-  dim3 grid((2 * D + 255) / 256);
-  if (dt == DT_BF16)
-    head_mod_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<const bf16 *>(head_table), temb,
-                                               head_mod, D);
-  else
-    head_mod_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(head_table), temb,
-                                                head_mod, D);
+    gemv_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(W), static_cast<const float *>(b),
+                                            x, (double)t, y, N, K, silu_in, fan, nfan, fan_out);
   return hipGetLastError();
 }
 
