@@ -76,16 +76,19 @@ constexpr int gemm_strip_floats() {
   return (32 * SROW * 4 > WN * TROW * (int)sizeof(T) ? 32 * SROW * 4 : WN * TROW * (int)sizeof(T)) / 4;
 }
 
-template <typename T, int BM, int BN, int EPI>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs &p, f32x16 (&acc)[BM / 64][BN / 64],
+// NWN waves along N, NW waves in all (NW / NWN along M); each wave owns a
+// WM x WN block as TM x TN 32x32 accumulators.
+template <typename T, int BM, int BN, int EPI, int NWN = 2, int NW = 4>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
+                                              f32x16 (&acc)[BM * NWN / NW / 32][BN / NWN / 32],
                                               float *scratch, int m0, int n0, const void *bias_g,
                                               int g) {
-  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+  constexpr int WM = BM * NWN / NW, WN = BN / NWN, TM = WM / 32, TN = WN / 32;
   constexpr int SROW = WN + 4;                        // fp32 strip row stride
   constexpr int TROW = 32 + 16 / (int)sizeof(T);      // transposed strip row stride
   constexpr int REG = gemm_strip_floats<T, WN>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int M = p.M, N = p.N;
   float *strip = scratch + wave * REG;
   T *stripT = reinterpret_cast<T *>(strip);
@@ -259,32 +262,34 @@ __device__ __forceinline__ void gemm_group(const GemmArgs &p, const void *&W, co
 // ---------------------------------------------------------------------------
 // Register-staged main loop (256x256 bf16; 64x64 fp32).
 // ---------------------------------------------------------------------------
-template <typename T, int BM, int BN, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
+template <typename T, int BM, int BN, int EPI, int NWN = 2, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_kernel(GemmArgs p) {
+  constexpr int NT = 64 * NW;           // threads
   constexpr int BK = 128 / sizeof(T);   // elements in a 128-byte row slice
   constexpr int VEC = 16 / sizeof(T);   // elements per 16-byte move
   constexpr int ROW = BK + VEC;         // LDS row stride (elements), 16-byte pad
   constexpr int CHUNKS = BK / 16;       // MFMA k-chunks per slice
-  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int WM = BM * NWN / NW, WN = BN / NWN;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int LA = BM / 32;           // 16-byte loads per thread per slice (A)
-  constexpr int LW = BN / 32;           // (W)
+  constexpr int RPP = NT / 8;           // rows one pass of 16-byte moves covers
+  constexpr int LA = BM / RPP;          // 16-byte loads per thread per slice (A)
+  constexpr int LW = BN / RPP;          // (W)
   typedef typename Frag<T>::type F;
 
   __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * ROW];
-  static_assert(4 * gemm_strip_floats<T, WN>() * 4 <= (int)sizeof(lds), "epilogue strips");
+  static_assert(NW * gemm_strip_floats<T, WN>() * 4 <= (int)sizeof(lds), "epilogue strips");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int M = p.M, N = p.N, K = p.K;
   int tm, tn;
   gemm_tile_of((N + BN - 1) / BN, (M + BM - 1) / BM, tm, tn);
   const int m0 = tm * BM;
   const int n0 = tn * BN;
 
-  // Each thread moves the 16-byte piece kk of rows (tid >> 3) + 32 i.
+  // Each thread moves the 16-byte piece kk of rows (tid >> 3) + RPP i.
   const int kk = (tid & 7) * VEC;
   const int r0 = tid >> 3;
   const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(p.A, (uint32_t)((int64_t)M * p.lda * sizeof(T)));
@@ -294,8 +299,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
   const __amdgpu_buffer_rsrc_t rw_src = make_rsrc(Wg, (uint32_t)((int64_t)N * p.ldw * sizeof(T)));
   const uint32_t a_off0 = (uint32_t)(((int64_t)(m0 + r0) * p.lda + kk) * sizeof(T));
   const uint32_t w_off0 = (uint32_t)(((int64_t)(n0 + r0) * p.ldw + kk) * sizeof(T));
-  const uint32_t a_step = (uint32_t)(32 * p.lda * sizeof(T));
-  const uint32_t w_step = (uint32_t)(32 * p.ldw * sizeof(T));
+  const uint32_t a_step = (uint32_t)(RPP * p.lda * sizeof(T));
+  const uint32_t w_step = (uint32_t)(RPP * p.ldw * sizeof(T));
 
   // Staging registers for one slice: pieces 0..LA-1 are A rows, LA.. are W rows.
   constexpr int NP = LA + LW;
@@ -310,7 +315,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
       stage[i] = buf_load16(rw_src, kin ? w_off0 + (i - LA) * w_step + kb : OOB);
   };
   auto sstore_piece = [&](int i, T *base) {
-    const int row = i < LA ? r0 + 32 * i : BM + r0 + 32 * (i - LA);
+    const int row = i < LA ? r0 + RPP * i : BM + r0 + RPP * (i - LA);
     *reinterpret_cast<U128 *>(base + row * ROW + kk) = stage[i];
   };
 
@@ -410,7 +415,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 
 
   __syncthreads();  // every wave is done with the main-loop buffers
-  gemm_epilogue<T, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0, bias_g, g);
+  gemm_epilogue<T, BM, BN, EPI, NWN, NW>(p, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0,
+                                          bias_g, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -563,15 +569,16 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   gemm_epilogue<bf16, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(lds), m0, n0, bias_g, g);
 }
 
-template <typename T, int BM, int BN>
+template <typename T, int BM, int BN, int NWN = 2, int NW = 4>
 static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
   dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM), a.gw ? a.groups : 1);
+  constexpr int NT = 64 * NW;
   switch (epi) {
-    case EPI_STORE: gemm_kernel<T, BM, BN, EPI_STORE><<<grid, 256, 0, s>>>(a); break;
-    case EPI_GELU: gemm_kernel<T, BM, BN, EPI_GELU><<<grid, 256, 0, s>>>(a); break;
-    case EPI_RESIDUAL: gemm_kernel<T, BM, BN, EPI_RESIDUAL><<<grid, 256, 0, s>>>(a); break;
-    case EPI_STORE_F32: gemm_kernel<T, BM, BN, EPI_STORE_F32><<<grid, 256, 0, s>>>(a); break;
-    case EPI_SPLIT: gemm_kernel<T, BM, BN, EPI_SPLIT><<<grid, 256, 0, s>>>(a); break;
+    case EPI_STORE: gemm_kernel<T, BM, BN, EPI_STORE, NWN, NW><<<grid, NT, 0, s>>>(a); break;
+    case EPI_GELU: gemm_kernel<T, BM, BN, EPI_GELU, NWN, NW><<<grid, NT, 0, s>>>(a); break;
+    case EPI_RESIDUAL: gemm_kernel<T, BM, BN, EPI_RESIDUAL, NWN, NW><<<grid, NT, 0, s>>>(a); break;
+    case EPI_STORE_F32: gemm_kernel<T, BM, BN, EPI_STORE_F32, NWN, NW><<<grid, NT, 0, s>>>(a); break;
+    case EPI_SPLIT: gemm_kernel<T, BM, BN, EPI_SPLIT, NWN, NW><<<grid, NT, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -597,13 +604,14 @@ bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) 
   return (M + 256) * lda * es < lim && (N + 256) * ldw * es < lim;
 }
 
-// Tile choice (measured on MI355X): 256x256 once the grid has at least half
-// a tile per CU, else 128x128 with at least one tile per CU, else 64x64.
+// Tile choice (measured on MI355X): 256x256 with 8 waves (two per SIMD, 3-15%
+// faster than 4 waves on every large step shape) once the grid has at least
+// half a tile per CU, else 128x128 with at least one tile per CU, else 64x64.
 static int pick_tile(int M, int N, int groups) {
   const int64_t G = groups > 1 ? groups : 1;
   const int64_t t256 = G * ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = G * ((M + 127) / 128) * ((N + 127) / 128);
-  if (t256 >= 128) return 1;
+  if (t256 >= 128) return 4;
   if (t128 >= 256) return 2;
   return 3;
 }
@@ -615,10 +623,13 @@ hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s,
   if (!gemm_offsets_fit(dt, a.M, a.lda, a.N, a.ldw)) return hipErrorInvalidValue;
   if (dt == DT_BF16) {
     if (tile == 0) tile = pick_tile(a.M, a.N, a.groups);
-    // a split store needs every wave's column strip inside one segment
-    while (epi == EPI_SPLIT && tile < 3 && a.seg_width % (tile == 1 ? 128 : 64) != 0) ++tile;
+    // a split store needs every wave's column strip inside one segment: 128
+    // columns for tile 1, 64 for tiles 2 and 4, 32 for tile 3
+    if (epi == EPI_SPLIT && tile == 1 && a.seg_width % 128 != 0) tile = 4;
+    if (epi == EPI_SPLIT && tile != 3 && a.seg_width % 64 != 0) tile = 3;
     switch (tile) {
       case 1: return launch_t<bf16, 256, 256>(epi, a, s);
+      case 4: return launch_t<bf16, 256, 256, 4, 8>(epi, a, s);
       case 2: return launch_dl<128, 128, 4>(epi, a, s);
       default: return launch_dl<64, 64, 5>(epi, a, s);
     }

@@ -47,7 +47,8 @@ struct GemmArgs {
   const void *const *gbias;
   int64_t seg_gstride[3];
 };
-// tile: 0 automatic, 1 256x256, 2 128x128, 3 64x64 (bf16); fp32 uses 64x64.
+// tile: 0 automatic, 1 256x256 (4 waves), 2 128x128, 3 64x64, 4 256x256 (8 waves)
+// (bf16); fp32 uses 64x64.
 hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile = 0);
 // Operand byte offsets are 32-bit: (rows + 256) * ld * element size < 2^31.
 bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw);

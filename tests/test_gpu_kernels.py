@@ -44,7 +44,7 @@ def _gemm_case(dtype, epi, M, N, K, tile, seed=0):
     return rel_l2(got, ref)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
 @pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
                                  B.DIT_EPI_STORE_F32])
 @pytest.mark.parametrize("M,N,K", [(1000, 700, 520), (300, 260, 64), (513, 1024, 1536)])
