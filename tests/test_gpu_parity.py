@@ -104,6 +104,8 @@ def _attention_case(cfg, sq, sk, v_const=None, rng=RNG):
     ("image_s_bf16", 1024, 1024), ("image_s_bf16", 1024, 256), ("image_s_bf16", 300, 1000),
     ("image_s_bf16", 1, 1), ("image_s_bf16", 129, 65),
     ("wan1p3b_bf16", 777, 1500), ("wan1p3b_bf16", 256, 512), ("wan1p3b_bf16", 64, 3),
+    # >= 256 workgroups of 256 queries: the two-query-block kernel (head_dim 128)
+    ("wan14b_bf16", 1700, 1000), ("wan14b_bf16", 1537, 64), ("image_l_bf16", 2400, 777),
 ])
 def test_attention_parity(name, sq, sk):
     require_gpu()
