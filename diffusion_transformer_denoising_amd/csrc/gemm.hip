@@ -442,9 +442,11 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, half = lane >> 5;
   const int M = p.M, N = p.N, K = p.K;
-  // small grids are resident all at once: plain row-major tile order
-  const int nx = (N + BN - 1) / BN;
-  const int m0 = (blockIdx.x / nx) * BM, n0 = (blockIdx.x % nx) * BN;
+  // XCD-aware tile order: even when the whole grid is resident at once, each
+  // XCD's L2 then holds only the A and W panels of its own block of tiles
+  int tm, tn;
+  gemm_tile_of((N + BN - 1) / BN, (M + BM - 1) / BM, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const i32x4 ars = buffer_words(p.A, (uint32_t)((int64_t)M * p.lda * 2));
   const void *Wg, *bias_g;
   int g;
@@ -606,13 +608,16 @@ bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) 
 
 // Tile choice (measured on MI355X): 256x256 with 8 waves (two per SIMD, 3-15%
 // faster than 4 waves on every large step shape) once the grid has at least
-// half a tile per CU, else 128x128 with at least one tile per CU, else 64x64.
-static int pick_tile(int M, int N, int groups) {
+// half a tile per CU; else 128x128 from half a tile per CU for the plain
+// epilogues (MLP-1 at 1024 tokens, 192 tiles: 3-6 % faster than 64x64) but
+// from one per CU for the split store with RoPE, whose heavier epilogue
+// favours more, smaller tiles; else 64x64.
+static int pick_tile(int M, int N, int groups, Epilogue epi) {
   const int64_t G = groups > 1 ? groups : 1;
   const int64_t t256 = G * ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = G * ((M + 127) / 128) * ((N + 127) / 128);
   if (t256 >= 128) return 4;
-  if (t128 >= 256) return 2;
+  if (t128 >= (epi == EPI_SPLIT ? 256 : 128)) return 2;
   return 3;
 }
 
@@ -622,7 +627,7 @@ hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s,
   if (a.gw ? (!a.gbias || a.groups < 1) : (a.W == nullptr || a.groups > 1)) return hipErrorInvalidValue;
   if (!gemm_offsets_fit(dt, a.M, a.lda, a.N, a.ldw)) return hipErrorInvalidValue;
   if (dt == DT_BF16) {
-    if (tile == 0) tile = pick_tile(a.M, a.N, a.groups);
+    if (tile == 0) tile = pick_tile(a.M, a.N, a.groups, epi);
     // a split store needs every wave's column strip inside one segment: 128
     // columns for tile 1, 64 for tiles 2 and 4, 32 for tile 3
     if (epi == EPI_SPLIT && tile == 1 && a.seg_width % 128 != 0) tile = 4;
