@@ -633,14 +633,18 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
 
 template <int HD>
 static hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
-  // waves per workgroup: the largest of 8, 4, 2, 1 that still gives >= 512 workgroups.
-  // 8 waves share each K/V tile among 256 queries (half the LDS fill traffic per
-  // MFMA); worth it on long key sequences only, where the fill is the steady state
-  // (measured: +2 % at 32760 keys, -11 % at 512).  A K tile must give every thread
-  // of the workgroup at least one 16-byte piece.
+  // Waves per workgroup: the largest of 8, 4, 2, 1 that still gives at least
+  // half a workgroup per CU.  The wave count is fixed by the queries (one per
+  // 32); more waves per workgroup share each K/V tile among more of them, so
+  // fewer tile loads, against fewer workgroups in flight (measured at 1024
+  // tokens, 12 heads: 2 waves and 192 workgroups 10 % faster than 1 and 384,
+  // 4 and 96 no faster).  8 waves share each tile among 256 queries (half the
+  // LDS fill traffic per MFMA); worth it on long key sequences only, where the
+  // fill is the steady state (measured: +2 % at 32760 keys, -11 % at 512).
+  // A K tile must give every thread of the workgroup at least one 16-byte piece.
   constexpr int MAXNW = HD >= 64 ? 8 : 4;
   int nw = MAXNW == 8 && a.sk >= 4096 ? 8 : 4;
-  while (nw > 1 && (int64_t)((a.sq + 32 * nw - 1) / (32 * nw)) * a.heads < 512) nw >>= 1;
+  while (nw > 1 && (int64_t)((a.sq + 32 * nw - 1) / (32 * nw)) * a.heads < 128) nw >>= 1;
   dim3 grid((a.sq + 32 * nw - 1) / (32 * nw), a.heads);
   if constexpr (MAXNW == 8) {
     if (nw == 8) {
