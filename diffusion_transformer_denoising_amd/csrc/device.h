@@ -80,12 +80,14 @@ __device__ __forceinline__ void dma_to_lds16(i32x4 rsrc, uint32_t lds_addr, uint
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // GELU, tanh form: z/2 (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3),
-// evaluated as z / (1 + exp(-2u)).
+// evaluated as z / (1 + exp(-2u)) with the hardware reciprocal (1 ulp; the
+// IEEE division sequence costs several times as much in the GEMM epilogue).
+// Limits stay exact: exp(-2u) = inf gives -0, exp(-2u) = 0 gives z.
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   float u = k0 * (z + 0.044715f * z * z * z);
   float e = fast_exp2(-2.0f * 1.4426950408889634f * u);
-  return z / (1.0f + e);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + fast_exp2(-1.4426950408889634f * z)); }
