@@ -162,8 +162,39 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
         }
       }
     } else {
-      constexpr int UPR = WN / 8;  // 8-column runs per strip row
-      for (int u = lane; u < 32 * UPR; u += 64) {
+      constexpr int UPR = WN / 8;              // 8-column runs per strip row
+      constexpr int NIT = 32 * UPR / 64;       // runs per lane
+      static_assert((32 * UPR) % 64 == 0, "whole runs per lane");
+      // First every global read of this lane's runs (the residual x, the RoPE
+      // table entries), then the stores: with a read and a store per run the
+      // compiler cannot move the next run's read above the store (they may
+      // alias), and each run would wait a full memory latency.
+      f32x4 pre[NIT][2];
+      if constexpr (EPI == EPI_RESIDUAL || EPI == EPI_SPLIT) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int u = lane + it * 64;
+          const int r = u / UPR, c8 = (u % UPR) * 8;
+          const int row = rowbase + r, col = colbase + c8;
+          if (row >= M || col >= N) continue;
+          if constexpr (EPI == EPI_RESIDUAL) {
+            if (vec_ok && N - col >= 8) {
+              const float *o = static_cast<const float *>(dst) + (int64_t)row * ld + col;
+              pre[it][0] = *reinterpret_cast<const f32x4 *>(o);
+              pre[it][1] = *reinterpret_cast<const f32x4 *>(o + 4);
+            }
+          } else if (rope) {
+            // pairs (2j, 2j+1) of the head; table column = channel / 2
+            const int ch0 = (segc + c8) % (2 * p.rope_half_d);
+            const int64_t t = (int64_t)row * p.rope_half_d + ch0 / 2;
+            pre[it][0] = *reinterpret_cast<const f32x4 *>(p.rope_cos + t);
+            pre[it][1] = *reinterpret_cast<const f32x4 *>(p.rope_sin + t);
+          }
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int u = lane + it * 64;
         const int r = u / UPR, c8 = (u % UPR) * 8;
         const int row = rowbase + r, col = colbase + c8;
         if (row >= M || col >= N) continue;
@@ -173,13 +204,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
         const f32x4 hi = *reinterpret_cast<const f32x4 *>(sp + 4);
         float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         if (EPI == EPI_SPLIT && rope) {
-          // pairs (2j, 2j+1) of the head; table column = channel / 2
-          const int ch0 = (segc + c8) % (2 * p.rope_half_d);
-          const float *ct = p.rope_cos + (int64_t)row * p.rope_half_d + ch0 / 2;
-          const float *st = p.rope_sin + (int64_t)row * p.rope_half_d + ch0 / 2;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float cs = ct[q], sn = st[q];
+            const float cs = pre[it][0][q], sn = pre[it][1][q];
             const float u0 = v[2 * q], u1 = v[2 * q + 1];
             v[2 * q] = u0 * cs - u1 * sn;
             v[2 * q + 1] = u0 * sn + u1 * cs;
@@ -189,7 +216,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
         if constexpr (EPI == EPI_RESIDUAL) {
           float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
           if (vec_ok && nvalid == 8) {
-            f32x4 x0 = *reinterpret_cast<f32x4 *>(o), x1 = *reinterpret_cast<f32x4 *>(o + 4);
+            f32x4 x0 = pre[it][0], x1 = pre[it][1];
 #pragma unroll
             for (int e = 0; e < 4; ++e) { x0[e] += v[e]; x1[e] += v[4 + e]; }
             *reinterpret_cast<f32x4 *>(o) = x0;
