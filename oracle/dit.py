@@ -291,6 +291,24 @@ def denoise_step(X, E, t: float, sigma: float, sigma_next: float, params: dict, 
     return euler_step(X, V, sigma, sigma_next), V
 
 
+def denoise_step_cfg(X, E, E_neg, t: float, sigma: float, sigma_next: float, guidance: float,
+                     params: dict, cfg):
+    """One denoise step with classifier-free guidance: (X_next, V).
+
+    The network runs twice on the same latents and timestep, once with the
+    positive embeddings E and once with the negative ones E_neg (page "Support
+    New Diffusion Models - SGLang Documentation": section 2 "Pipeline Config",
+    the positive and negative condition kwargs; section 1 "Sampling Params",
+    guidance_scale; section 4, the DenoisingStage field table,
+    negative_prompt_embeds when CFG is used).  Reading (the pages print no
+    formula): the guided velocity is V_neg + g (V_pos - V_neg), followed by the
+    same Euler update as the unguided step."""
+    V_pos = dit_forward(X, E, t, params, cfg)
+    V_neg = dit_forward(X, E_neg, t, params, cfg)
+    V = V_neg + float(guidance) * (V_pos - V_neg)
+    return euler_step(X, V, sigma, sigma_next), V
+
+
 def sample(X0, E, params: dict, cfg, n_steps: int, shift: float, first_steps=None):
     """Run the schedule from X0; returns X after ``first_steps`` steps (all
     when None)."""

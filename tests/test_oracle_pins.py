@@ -376,3 +376,52 @@ def test_forward_identity_blocks_reduce_to_embed_and_head():
     x = oracle.patchify(X0, cfg.patch) @ g["pe_w"].T + g["pe_b"]
     temb, _ = oracle.time_embedding(t, g, cfg.freq_dim)
     np.testing.assert_allclose(u, oracle.final_layer(x, temb, g, cfg), atol=1e-13)
+
+
+# ----------------------------------------------------------------- guidance
+def _cfg_case(blocks=2):
+    cfg = tiny_cfg()
+    params = _tiny_params(cfg, blocks=blocks)
+    X0 = RNG.normal(0, 1, (cfg.in_channels,) + cfg.latent)
+    E = RNG.normal(0, 1, (3, cfg.text_dim))
+    En = RNG.normal(0, 1, (3, cfg.text_dim))
+    return cfg, params, X0, E, En
+
+
+def test_cfg_equal_embeddings_is_the_unguided_step():
+    # Same embeddings on both sides: the guidance term vanishes for every scale
+    # (catches a scale applied to X or to one branch only, or branches that
+    # see each other's context).
+    cfg, params, X0, E, _ = _cfg_case()
+    X1, V1 = oracle.denoise_step(X0, E, 700.0, 0.7, 0.6, params, cfg)
+    for g in (0.0, 1.0, 4.0, -2.5):
+        X2, V2 = oracle.denoise_step_cfg(X0, E, E, 700.0, 0.7, 0.6, g, params, cfg)
+        np.testing.assert_array_equal(V2, V1)
+        np.testing.assert_array_equal(X2, X1)
+
+
+def test_cfg_scales_zero_and_one_select_a_branch():
+    # g = 0 is the negative branch exactly, g = 1 the positive one (catches the
+    # two embeddings swapped or the difference taken the wrong way round).
+    cfg, params, X0, E, En = _cfg_case()
+    _, Vp = oracle.denoise_step(X0, E, 400.0, 0.4, 0.3, params, cfg)
+    _, Vn = oracle.denoise_step(X0, En, 400.0, 0.4, 0.3, params, cfg)
+    assert np.max(np.abs(Vp - Vn)) > 1e-3  # the two contexts do differ
+    _, V0 = oracle.denoise_step_cfg(X0, E, En, 400.0, 0.4, 0.3, 0.0, params, cfg)
+    np.testing.assert_array_equal(V0, Vn)
+    _, V1 = oracle.denoise_step_cfg(X0, E, En, 400.0, 0.4, 0.3, 1.0, params, cfg)
+    np.testing.assert_allclose(V1, Vp, rtol=0, atol=1e-14)
+
+
+def test_cfg_affine_in_the_scale():
+    # The guided velocity is affine in g with slope V_pos - V_neg (catches a
+    # scale applied twice, squared, or folded into the Euler step size).
+    cfg, params, X0, E, En = _cfg_case()
+    Vs = {g: oracle.denoise_step_cfg(X0, E, En, 250.0, 0.25, 0.2, g, params, cfg)[1]
+          for g in (1.0, 2.0, 3.0)}
+    _, Vp = oracle.denoise_step(X0, E, 250.0, 0.25, 0.2, params, cfg)
+    _, Vn = oracle.denoise_step(X0, En, 250.0, 0.25, 0.2, params, cfg)
+    np.testing.assert_allclose(Vs[3.0] - Vs[2.0], Vs[2.0] - Vs[1.0], atol=1e-13)
+    np.testing.assert_allclose(Vs[2.0] - Vs[1.0], Vp - Vn, atol=1e-13)
+    X4, V4 = oracle.denoise_step_cfg(X0, E, En, 250.0, 0.25, 0.2, 4.0, params, cfg)
+    np.testing.assert_allclose(X4, X0 + (0.2 - 0.25) * V4, atol=1e-15)
