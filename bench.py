@@ -1,14 +1,16 @@
 """Benchmark: denoise steps per second of one DiT denoising step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--calibrate-copy]
+                    [--guidance G] [--no-cpu-baseline] [--calibrate-copy]
 
 A step is one call of dit_denoise_step: time embedding, context projection,
 patch embedding, every DiT block (LayerNorm+adaLN, QKV projection, RoPE,
 self-attention, gated output projection, cross-attention, GELU MLP) and the
 head, then the fused unpatchify + Euler update.  Inputs and weights are seeded
 synthetic data already resident in HBM when timing starts; the timestep and
-sigmas cycle through the workload's flow schedule.
+sigmas cycle through the workload's flow schedule.  With --guidance G a step is
+one call of dit_denoise_step_cfg instead: both branches (positive context and
+a second, negative one) as one batch of two sequences, guidance scale G.
 
 Prints ONE JSON line on stdout (diagnostics go to stderr):
   value          whole-job steps/s (K timed steps, bracketed by
@@ -52,31 +54,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kind_work(cfg) -> dict:
+def kind_work(cfg, nb: int = 1) -> dict:
     """Algorithmic work per launch of each kernel kind: ("flop", n) for matrix-core
-    kernels, ("byte", n) for bandwidth-bound ones (minimum HBM traffic)."""
+    kernels, ("byte", n) for bandwidth-bound ones (minimum HBM traffic).  nb = 2
+    is the guided step: the block kernels and the head process two stacked
+    sequences per launch, the context kernels run once per context."""
     S, D, F, L, P = cfg.tokens, cfg.hidden, cfg.mlp_hidden, cfg.ctx_len, cfg.patch_dim
+    R = nb * S
     es = 2 if cfg.dtype == "bf16" else 4
     n_lat = cfg.latent_numel
     return {
-        "gemm_qkv_rope": ("flop", 2 * S * D * 3 * D),
-        "gemm_o": ("flop", 2 * S * D * D),
-        "gemm_cross_q": ("flop", 2 * S * D * D),
-        # one grouped launch per step computes every block's cross K / V^T
+        "gemm_qkv_rope": ("flop", 2 * R * D * 3 * D),
+        "gemm_o": ("flop", 2 * R * D * D),
+        "gemm_cross_q": ("flop", 2 * R * D * D),
+        # one grouped launch per context computes every block's cross K / V^T
         "gemm_cross_kv": ("flop", cfg.num_blocks * 2 * L * D * 2 * D),
-        "gemm_cross_o": ("flop", 2 * S * D * D),
-        "gemm_mlp1_gelu": ("flop", 2 * S * D * F),
-        "gemm_mlp2": ("flop", 2 * S * F * D),
+        "gemm_cross_o": ("flop", 2 * R * D * D),
+        "gemm_mlp1_gelu": ("flop", 2 * R * D * F),
+        "gemm_mlp2": ("flop", 2 * R * F * D),
         "gemm_text_proj": ("flop", 2 * L * cfg.text_dim * D),
         "gemm_patch_embed": ("flop", 2 * S * P * D),
-        "gemm_head": ("flop", 2 * S * D * P),
-        "attention_self": ("flop", 4 * S * S * D),
-        "attention_cross": ("flop", 4 * S * L * D),
+        "gemm_head": ("flop", 2 * R * D * P),
+        "attention_self": ("flop", nb * 4 * S * S * D),
+        "attention_cross": ("flop", nb * 4 * S * L * D),
         # read the fp32 row, write the normalised row
-        "layernorm_modulate": ("byte", S * D * (4 + es)),
+        "layernorm_modulate": ("byte", R * D * (4 + es)),
         "patchify": ("byte", n_lat * (4 + es)),
-        # read velocity tokens, read-modify-write the latents
-        "unpatchify_euler": ("byte", n_lat * 4 * 3),
+        # read the velocity tokens (of each branch), read-modify-write the latents
+        "unpatchify_euler": ("byte", n_lat * 4 * (nb + 2)),
         # three GEMV launches per step; the per-launch figure is their mean
         "time_embedding": ("byte", es * (cfg.freq_dim * D + D * D + 6 * D * D) // 3),
     }
@@ -103,9 +108,10 @@ def measured_traffic(kernel_kind: str, workload: str):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(cfg, prm, X0, E, budget_s: float = 20.0) -> dict:
+def cpu_baseline(cfg, prm, X0, E, budget_s: float = 20.0, E_neg=None, g=None) -> dict:
     """The oracle as it stands, timed on the host cores over the first steps of
-    the same chain (as many as fit the budget, at least one)."""
+    the same chain (as many as fit the budget, at least one); with E_neg and g,
+    the oracle's guided step."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -118,14 +124,17 @@ def cpu_baseline(cfg, prm, X0, E, budget_s: float = 20.0) -> dict:
     t0 = time.perf_counter()
     while done < cfg.steps:
         t = float(np.float32(1000.0 * sig[done]))
-        X, _ = oracle.denoise_step(X, E, t, sig[done], sig[done + 1], prm, cfg)
+        if E_neg is None:
+            X, _ = oracle.denoise_step(X, E, t, sig[done], sig[done + 1], prm, cfg)
+        else:
+            X, _ = oracle.denoise_step_cfg(X, E, E_neg, t, sig[done], sig[done + 1], g, prm, cfg)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {done} of the {cfg.steps} denoise steps of {cfg.name}, float64 numpy "
-                      f"oracle, {dt:.1f} s"}
+            "sample": f"first {done} of the {cfg.steps} {'guided ' if E_neg is not None else ''}"
+                      f"denoise steps of {cfg.name}, float64 numpy oracle, {dt:.1f} s"}
 
 
 def main(argv=None) -> int:
@@ -134,6 +143,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--guidance", type=float, default=None,
+                    help="time the guided step (classifier-free guidance) at this scale")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (the known-size kernel "
@@ -169,10 +180,14 @@ def main(argv=None) -> int:
     prm = SP.make_params(cfg)
     X0 = SP.make_latents(cfg)
     E = SP.make_ctx(cfg)
+    guided = args.guidance is not None
+    nb = 2 if guided else 1
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-    m = DeviceDiT(cfg, prm)
+    m = DeviceDiT(cfg, prm, guidance=guided)
     X = torch.from_numpy(X0).cuda()
     Ed = torch.from_numpy(E).cuda().to(torch_dtype(cfg))
+    # the negative context of a guided step: its own seed (3)
+    End = torch.from_numpy(SP.make_ctx(cfg, seed=3)).cuda().to(torch_dtype(cfg)) if guided else None
     sig = B.dit_flow_sigmas(cfg.steps, cfg.shift)
     sched = [(float(np.float32(1000.0 * sig[k])), float(sig[k]), float(sig[k + 1]))
              for k in range(cfg.steps)]
@@ -180,7 +195,10 @@ def main(argv=None) -> int:
     def run(n, k0=0):
         for i in range(n):
             t, s0, s1 = sched[(k0 + i) % cfg.steps]
-            m.denoise_step(X, Ed, t, s0, s1)
+            if guided:
+                m.denoise_step_cfg(X, Ed, End, t, s0, s1, args.guidance)
+            else:
+                m.denoise_step(X, Ed, t, s0, s1)
 
     run(args.warmup)
     torch.cuda.synchronize()
@@ -203,7 +221,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     B.dit_profile_enable(m.handle, False)
     prof = B.profile_summary(m.handle)
-    work = kind_work(cfg)
+    work = kind_work(cfg, nb)
     kernels = {}
     for name, (n, tms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
         unit, amount = work.get(name, ("flop", 0))
@@ -256,6 +274,11 @@ def main(argv=None) -> int:
                           "event_pair_overhead_us": round(overhead_ms * 1e3, 3), "source": src}
 
     fl = cfg.flops_per_step()
+    if guided:
+        # both branches, except the patch embedding and the time path (shared)
+        shared = 2 * cfg.tokens * cfg.patch_dim * cfg.hidden + fl["time"]
+        fl = {k: (2 * v if k != "time" else v) for k, v in fl.items()}
+        fl["total"] -= shared
     out = {
         "metric": METRIC,
         "value": round(1e3 / ms_per_step, 4),
@@ -274,7 +297,8 @@ def main(argv=None) -> int:
                    "mlp_hidden": cfg.mlp_hidden, "ctx_len": cfg.ctx_len,
                    "text_dim": cfg.text_dim, "latent": list(cfg.latent_shape),
                    "schedule_steps": cfg.steps, "shift": cfg.shift, "batch": 1,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   **({"guidance_scale": args.guidance, "sequences": 2} if guided else {})},
         "step_tflops": round(fl["total"] / (ms_per_step / 1e3) / 1e12, 2),
         "step_frac_of_peak": round(fl["total"] / (ms_per_step / 1e3) / 1e12 / peak, 4),
         "attention": {"tflops": round(att_tf, 2), "frac_of_peak": round(att_tf / peak, 4)},
@@ -284,7 +308,9 @@ def main(argv=None) -> int:
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same workload")
-        out["cpu_baseline"] = cpu_baseline(cfg, prm, X0, E)
+        out["cpu_baseline"] = (cpu_baseline(cfg, prm, X0, E, E_neg=SP.make_ctx(cfg, seed=3),
+                                            g=args.guidance) if guided else
+                               cpu_baseline(cfg, prm, X0, E))
     else:
         out["cpu_baseline"] = None
     m.close()

@@ -33,7 +33,8 @@ class dit_config(ctypes.Structure):
     _fields_ = [(n, c_i32) for n in (
         "num_blocks", "hidden", "heads", "head_dim", "mlp_hidden", "freq_dim", "in_channels",
         "patch_f", "patch_h", "patch_w", "lat_f", "lat_h", "lat_w", "rope_f", "rope_h", "rope_w",
-        "ctx_len_max", "text_dim")] + [("rope_theta", c_f32), ("ln_eps", c_f32), ("dtype", c_i32)]
+        "ctx_len_max", "text_dim")] + [("rope_theta", c_f32), ("ln_eps", c_f32), ("dtype", c_i32),
+                                       ("guidance", c_i32)]
 
 
 GLOBAL_FIELDS = ("t1_w", "t1_b", "t2_w", "t2_b", "mod_w", "mod_b", "txt_w", "txt_b",
@@ -69,6 +70,8 @@ _SIGS = {
     "dit_destroy": ([c_vp], c_i32),
     "dit_block_forward": ([c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp], c_i32),
     "dit_denoise_step": ([c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_f32, c_vp, c_vp], c_i32),
+    "dit_denoise_step_cfg": ([c_vp, c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_f32, c_f32, c_vp,
+                              c_vp], c_i32),
     "dit_euler_step": ([c_vp, c_vp, c_i64, c_f32, c_f32, c_vp], c_i32),
     "dit_flow_sigmas": ([c_i32, c_f64, ctypes.POINTER(c_f64)], c_i32),
     "dit_attention": ([c_i32, c_i32, c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64,
@@ -122,11 +125,13 @@ def dit_status_string(status: int) -> str:
     return status_string(status)
 
 
-def make_config(cfg) -> dit_config:
+def make_config(cfg, guidance: bool = False) -> dit_config:
     """dit_config from any object with the workload attributes (hidden, heads,
     head_dim, mlp_hidden, num_blocks, in_channels, patch, latent, rope,
-    ctx_len, text_dim, freq_dim, rope_theta, ln_eps, dtype)."""
+    ctx_len, text_dim, freq_dim, rope_theta, ln_eps, dtype); guidance sizes
+    the workspace for guided steps."""
     c = dit_config()
+    c.guidance = 1 if guidance else 0
     c.num_blocks, c.hidden, c.heads, c.head_dim = cfg.num_blocks, cfg.hidden, cfg.heads, cfg.head_dim
     c.mlp_hidden, c.freq_dim, c.in_channels = cfg.mlp_hidden, cfg.freq_dim, cfg.in_channels
     c.patch_f, c.patch_h, c.patch_w = cfg.patch
@@ -165,6 +170,13 @@ def dit_denoise_step(handle: int, X: int, ctx: int, ctx_len: int, t: float, sigm
                      sigma_next: float, v_out: int | None = None, stream: int = 0) -> None:
     _check(lib().dit_denoise_step(handle, X, ctx, ctx_len, t, sigma, sigma_next, v_out, stream),
            "dit_denoise_step")
+
+
+def dit_denoise_step_cfg(handle: int, X: int, ctx: int, ctx_neg: int, ctx_len: int, t: float,
+                         sigma: float, sigma_next: float, guidance_scale: float,
+                         v_out: int | None = None, stream: int = 0) -> None:
+    _check(lib().dit_denoise_step_cfg(handle, X, ctx, ctx_neg, ctx_len, t, sigma, sigma_next,
+                                      guidance_scale, v_out, stream), "dit_denoise_step_cfg")
 
 
 def dit_euler_step(X: int, v: int, n: int, sigma: float, sigma_next: float, stream: int = 0) -> None:

@@ -29,6 +29,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace plan: every buffer the step needs, at 256-byte aligned offsets.
 struct Plan {
   int64_t S, S_pad, L_pad, P, D, F, H, d;
+  int64_t NB;  // sequences the activation buffers hold: 2 with guidance, else 1
   size_t es;  // element size
   // kc, vct hold the cross K / V^T of every block: [B][L_max][D], [B][D][L_pad];
   // gtab is a device table of weight pointers: ckv_w[0..B), ckv_b[0..B) (the
@@ -49,27 +50,31 @@ bool plan_layout(const dit_config &c, Plan &p) {
   p.S_pad = (int64_t)round_up((size_t)p.S, 64);
   p.L_pad = (int64_t)round_up((size_t)c.ctx_len_max, 64);
   p.P = (int64_t)c.in_channels * c.patch_f * c.patch_h * c.patch_w;
+  p.NB = c.guidance ? 2 : 1;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
     off = round_up(off + bytes, WS_ALIGN);
     return at;
   };
-  const size_t f4 = 4, es = p.es;
+  const size_t f4 = 4, es = p.es, NB = (size_t)p.NB;
+  // sequences stacked: rows [n S, (n+1) S) of x, y, q, k, o, h, u are sequence
+  // n; vt columns [n S_pad, (n+1) S_pad); c, kc, vct hold context n at n times
+  // their one-context size
   p.cos_t = take(f4 * p.S * (p.d / 2));
   p.sin_t = take(f4 * p.S * (p.d / 2));
-  p.x = take(f4 * p.S * p.D);
-  p.y = take(es * p.S * p.D);
-  p.q = take(es * p.S * p.D);
-  p.k = take(es * p.S * p.D);
-  p.vt = take(es * p.D * p.S_pad);
-  p.o = take(es * p.S * p.D);
-  p.h = take(es * p.S * p.F);
-  p.c = take(es * (size_t)c.ctx_len_max * p.D);
-  p.kc = take(es * (size_t)c.num_blocks * c.ctx_len_max * p.D);
-  p.vct = take(es * (size_t)c.num_blocks * p.D * p.L_pad);
+  p.x = take(f4 * NB * p.S * p.D);
+  p.y = take(es * NB * p.S * p.D);
+  p.q = take(es * NB * p.S * p.D);
+  p.k = take(es * NB * p.S * p.D);
+  p.vt = take(es * p.D * NB * p.S_pad);
+  p.o = take(es * NB * p.S * p.D);
+  p.h = take(es * NB * p.S * p.F);
+  p.c = take(es * NB * (size_t)c.ctx_len_max * p.D);
+  p.kc = take(es * NB * (size_t)c.num_blocks * c.ctx_len_max * p.D);
+  p.vct = take(es * NB * (size_t)c.num_blocks * p.D * p.L_pad);
   p.patches = take(es * p.S * p.P);
-  p.u = take(f4 * p.S * p.P);
+  p.u = take(f4 * NB * p.S * p.P);
   p.h1 = take(f4 * p.D);
   p.temb = take(f4 * p.D);
   p.e = take(f4 * 6 * p.D);
@@ -104,8 +109,13 @@ dit_status check_config(const dit_config *c) {
   const int64_t S = (int64_t)(c->lat_f / c->patch_f) * (c->lat_h / c->patch_h) *
                     (c->lat_w / c->patch_w);
   if (S > (int64_t)1 << 30) return DIT_ERR_UNSUPPORTED;
+  if (c->guidance != 0 && c->guidance != 1) return DIT_ERR_INVALID_ARG;
+  // guided steps stack two sequences; the transposed values are written in
+  // runs of 8 rows, which must not straddle them
+  if (c->guidance && S % 8) return DIT_ERR_UNSUPPORTED;
+  const int64_t rows = c->guidance ? 2 * S : S;
   const DType dt = c->dtype == DIT_BF16 ? DT_BF16 : DT_F32;
-  if (!gemm_offsets_fit(dt, S, c->mlp_hidden, 3 * (int64_t)c->hidden, c->mlp_hidden) ||
+  if (!gemm_offsets_fit(dt, rows, c->mlp_hidden, 3 * (int64_t)c->hidden, c->mlp_hidden) ||
       !gemm_offsets_fit(dt, c->ctx_len_max, c->text_dim, c->mlp_hidden, c->hidden))
     return DIT_ERR_UNSUPPORTED;
   return DIT_OK;
@@ -217,47 +227,60 @@ GemmArgs gemm(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int
   return a;
 }
 
-// One block on the residual stream x [S, D] with projected context ctx [L, D].
+// One block on the residual stream x [nb S, D] (nb stacked sequences sharing
+// the modulation) with projected context ctx [L, D] (one sequence, computed
+// here) or, with ckv_ready, the cross K / V^T of context n already in slot n
+// of kc / vct.
 dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, const float *mod,
-                     hipStream_t s, bool ckv_ready) {
+                     hipStream_t s, bool ckv_ready, int nb) {
   const dit_config &c = m->cfg;
   const Plan &p = m->plan;
   const dit_block_weights &w = m->blocks[b];
-  const int S = (int)p.S, D = (int)p.D, F = (int)p.F;
+  const int S = (int)p.S, D = (int)p.D, F = (int)p.F, R = nb * S;
+  const int B = c.num_blocks;
   void *y = m->buf<void>(p.y), *q = m->buf<void>(p.q), *k = m->buf<void>(p.k);
   void *vt = m->buf<void>(p.vt), *o = m->buf<void>(p.o), *h = m->buf<void>(p.h);
-  // this block's cross K / V^T slots
+  // this block's cross K / V^T slots (context 0; context n at n * ctx_k / ctx_v)
   void *kc = m->buf<char>(p.kc) + p.es * (size_t)b * c.ctx_len_max * p.D;
   void *vct = m->buf<char>(p.vct) + p.es * (size_t)b * p.D * p.L_pad;
+  const int64_t ctx_k = (int64_t)B * c.ctx_len_max * D, ctx_v = (int64_t)B * D * p.L_pad;
+  const int64_t vt_ld = nb * p.S_pad;  // the sequences' values side by side
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
 
   // self-attention branch: y = LN(x)(1 + scale_a) + shift_a
-  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, mod + 0 * D, mod + 1 * D, y, s));
+  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, R, D, c.ln_eps, mod + 0 * D, mod + 1 * D, y, s));
   {
-    GemmArgs a = gemm(y, D, w.qkv_w, D, S, 3 * D, D, w.qkv_b);
+    GemmArgs a = gemm(y, D, w.qkv_w, D, R, 3 * D, D, w.qkv_b);
     a.seg_width = D;
     a.seg_ptr[0] = q; a.seg_ld[0] = D; a.seg_trans[0] = 0;
     a.seg_ptr[1] = k; a.seg_ld[1] = D; a.seg_trans[1] = 0;
-    a.seg_ptr[2] = vt; a.seg_ld[2] = p.S_pad; a.seg_trans[2] = 1;
+    a.seg_ptr[2] = vt; a.seg_ld[2] = vt_ld; a.seg_trans[2] = 1;
     // RoPE on q and k inside the projection's epilogue
     a.seg_rope[0] = 1; a.seg_rope[1] = 1;
     a.rope_cos = m->buf<float>(p.cos_t); a.rope_sin = m->buf<float>(p.sin_t);
     a.rope_half_d = c.head_dim / 2;
+    if (nb > 1) {
+      a.seg_rows = S;
+      a.seg_bstride = p.S_pad;
+    }
     DIT_RUN(m, PK_GEMM_QKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
   }
   {
-    AttnArgs a{q, D, k, D, vt, p.S_pad, o, D, S, S, c.heads, c.head_dim, scale_log2};
+    AttnArgs a{q, D, k, D, vt, vt_ld, o, D, S, S, c.heads, c.head_dim, scale_log2};
+    a.batch = nb;
+    a.bq = a.bk = a.bo = (int64_t)S * D;
+    a.bvt = p.S_pad;
     DIT_RUN(m, PK_ATTN_SELF, s, launch_attention(m->dt, a, s));
   }
   {
-    GemmArgs a = gemm(o, D, w.o_w, D, S, D, D, w.o_b);
+    GemmArgs a = gemm(o, D, w.o_w, D, R, D, D, w.o_b);
     a.out = x; a.ldo = D; a.gate = mod + 2 * D;
     DIT_RUN(m, PK_GEMM_O, s, launch_gemm(m->dt, EPI_RESIDUAL, a, s));
   }
   // cross-attention branch (plain LN, ungated)
-  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, nullptr, nullptr, y, s));
+  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, R, D, c.ln_eps, nullptr, nullptr, y, s));
   {
-    GemmArgs a = gemm(y, D, w.cq_w, D, S, D, D, w.cq_b);
+    GemmArgs a = gemm(y, D, w.cq_w, D, R, D, D, w.cq_b);
     a.out = q; a.ldo = D;
     DIT_RUN(m, PK_GEMM_CQ, s, launch_gemm(m->dt, EPI_STORE, a, s));
   }
@@ -270,22 +293,26 @@ dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, cons
   }
   {
     AttnArgs a{q, D, kc, D, vct, p.L_pad, o, D, S, L, c.heads, c.head_dim, scale_log2};
+    a.batch = nb;
+    a.bq = a.bo = (int64_t)S * D;
+    a.bk = ctx_k;
+    a.bvt = ctx_v;
     DIT_RUN(m, PK_ATTN_CROSS, s, launch_attention(m->dt, a, s));
   }
   {
-    GemmArgs a = gemm(o, D, w.co_w, D, S, D, D, w.co_b);
+    GemmArgs a = gemm(o, D, w.co_w, D, R, D, D, w.co_b);
     a.out = x; a.ldo = D; a.gate = nullptr;
     DIT_RUN(m, PK_GEMM_CO, s, launch_gemm(m->dt, EPI_RESIDUAL, a, s));
   }
   // MLP branch: y = LN(x)(1 + scale_f) + shift_f; x += gate_f * W2 gelu(W1 y + b1) + b2
-  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, mod + 3 * D, mod + 4 * D, y, s));
+  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, R, D, c.ln_eps, mod + 3 * D, mod + 4 * D, y, s));
   {
-    GemmArgs a = gemm(y, D, w.w1, D, S, F, D, w.b1);
+    GemmArgs a = gemm(y, D, w.w1, D, R, F, D, w.b1);
     a.out = h; a.ldo = F;
     DIT_RUN(m, PK_GEMM_MLP1, s, launch_gemm(m->dt, EPI_GELU, a, s));
   }
   {
-    GemmArgs a = gemm(h, F, w.w2, F, S, D, F, w.b2);
+    GemmArgs a = gemm(h, F, w.w2, F, R, D, F, w.b2);
     a.out = x; a.ldo = D; a.gate = mod + 5 * D;
     DIT_RUN(m, PK_GEMM_MLP2, s, launch_gemm(m->dt, EPI_RESIDUAL, a, s));
   }
@@ -388,33 +415,40 @@ dit_status dit_block_forward(dit_model *m, int32_t block, float *x, const void *
   if (!m || !ok_ptr(x) || !ok_ptr(ctx) || !ok_ptr(mod)) return DIT_ERR_INVALID_ARG;
   if (block < 0 || block >= m->cfg.num_blocks) return DIT_ERR_SHAPE;
   if (ctx_len < 1 || ctx_len > m->cfg.ctx_len_max) return DIT_ERR_SHAPE;
-  return run_block(m, block, x, ctx, ctx_len, mod, static_cast<hipStream_t>(stream), false);
+  return run_block(m, block, x, ctx, ctx_len, mod, static_cast<hipStream_t>(stream), false, 1);
 }
 
-dit_status dit_denoise_step(dit_model *m, float *X, const void *ctx, int32_t ctx_len, float t,
-                            float sigma, float sigma_next, float *v_out, void *stream) {
-  if (!m || !ok_ptr(X) || !ok_ptr(ctx)) return DIT_ERR_INVALID_ARG;
-  if (v_out && !aligned16(v_out)) return DIT_ERR_INVALID_ARG;
-  if (!std::isfinite(t) || !std::isfinite(sigma) || !std::isfinite(sigma_next))
-    return DIT_ERR_INVALID_ARG;
-  if (ctx_len < 1 || ctx_len > m->cfg.ctx_len_max) return DIT_ERR_SHAPE;
+}  // extern "C"
+
+namespace {
+
+// One denoise step over nb sequences that share the latents X and the
+// timestep and differ in their context: ctx[n] for sequence n.  nb = 2 is the
+// guided step: sequence 0 takes the positive embeddings, 1 the negative ones,
+// and the Euler update uses v_neg + g (v_pos - v_neg).
+dit_status run_step(dit_model *m, float *X, const void *const *ctx, int nb, int ctx_len, float t,
+                    float sigma, float sigma_next, float g, float *v_out, hipStream_t s) {
   const dit_config &c = m->cfg;
   const Plan &p = m->plan;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int S = (int)p.S, D = (int)p.D, P = (int)p.P;
+  const int S = (int)p.S, D = (int)p.D, P = (int)p.P, R = nb * S, B = c.num_blocks;
   float *bmod = m->buf<float>(p.bmod), *hmod = m->buf<float>(p.hmod);
   float *temb = m->buf<float>(p.temb), *x = m->buf<float>(p.x), *u = m->buf<float>(p.u);
 
   dit_status st = run_time_path(m, t, bmod, hmod, temb, s);
   if (st != DIT_OK) return st;
 
-  const void *cproj = ctx;
+  // projected context n at c + n * L_max * D (or the caller's tokens)
+  const void *cproj[2] = {ctx[0], nb > 1 ? ctx[1] : nullptr};
   if (c.text_dim != c.hidden) {
-    GemmArgs a = gemm(ctx, c.text_dim, m->g.txt_w, c.text_dim, ctx_len, D, c.text_dim, m->g.txt_b);
-    a.out = m->buf<void>(p.c);
-    a.ldo = D;
-    DIT_RUN(m, PK_GEMM_TXT, s, launch_gemm(m->dt, EPI_STORE, a, s));
-    cproj = m->buf<void>(p.c);
+    for (int n = 0; n < nb; ++n) {
+      void *cn = m->buf<char>(p.c) + p.es * (size_t)n * c.ctx_len_max * D;
+      GemmArgs a = gemm(ctx[n], c.text_dim, m->g.txt_w, c.text_dim, ctx_len, D, c.text_dim,
+                        m->g.txt_b);
+      a.out = cn;
+      a.ldo = D;
+      DIT_RUN(m, PK_GEMM_TXT, s, launch_gemm(m->dt, EPI_STORE, a, s));
+      cproj[n] = cn;
+    }
   }
   DIT_RUN(m, PK_PATCHIFY, s, launch_patchify(m->dt, X, m->buf<void>(p.patches), c.in_channels, c.lat_f, c.lat_h,
                           c.lat_w, c.patch_f, c.patch_h, c.patch_w, s));
@@ -424,34 +458,78 @@ dit_status dit_denoise_step(dit_model *m, float *X, const void *ctx, int32_t ctx
     a.ldo = D;
     DIT_RUN(m, PK_GEMM_PE, s, launch_gemm(m->dt, EPI_STORE_F32, a, s));
   }
-  // cross K / V^T of every block in one grouped launch: they depend on the
-  // context only, not on the residual stream
-  {
-    GemmArgs a = gemm(cproj, D, nullptr, D, ctx_len, 2 * D, D, nullptr);
+  // every sequence starts from the same embedded latents
+  for (int n = 1; n < nb; ++n)
+    DIT_TRY(hipMemcpyAsync(x + (size_t)n * S * D, x, sizeof(float) * (size_t)S * D,
+                           hipMemcpyDeviceToDevice, s));
+  // cross K / V^T of every block in one grouped launch per context: they
+  // depend on the context only, not on the residual stream
+  for (int n = 0; n < nb; ++n) {
+    GemmArgs a = gemm(cproj[n], D, nullptr, D, ctx_len, 2 * D, D, nullptr);
     a.seg_width = D;
-    a.seg_ptr[0] = m->buf<void>(p.kc); a.seg_ld[0] = D; a.seg_trans[0] = 0;
-    a.seg_ptr[1] = m->buf<void>(p.vct); a.seg_ld[1] = p.L_pad; a.seg_trans[1] = 1;
-    a.groups = c.num_blocks;
+    a.seg_ptr[0] = m->buf<char>(p.kc) + p.es * (size_t)n * B * c.ctx_len_max * D;
+    a.seg_ld[0] = D; a.seg_trans[0] = 0;
+    a.seg_ptr[1] = m->buf<char>(p.vct) + p.es * (size_t)n * B * D * p.L_pad;
+    a.seg_ld[1] = p.L_pad; a.seg_trans[1] = 1;
+    a.groups = B;
     a.gw = m->buf<const void *>(p.gtab);
-    a.gbias = m->buf<const void *>(p.gtab) + c.num_blocks;
+    a.gbias = m->buf<const void *>(p.gtab) + B;
     a.seg_gstride[0] = (int64_t)c.ctx_len_max * D;
     a.seg_gstride[1] = (int64_t)D * p.L_pad;
     DIT_RUN(m, PK_GEMM_CKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
   }
-  for (int b = 0; b < c.num_blocks; ++b) {
-    st = run_block(m, b, x, cproj, ctx_len, bmod + (int64_t)b * 6 * D, s, true);
+  for (int b = 0; b < B; ++b) {
+    st = run_block(m, b, x, nullptr, ctx_len, bmod + (int64_t)b * 6 * D, s, true, nb);
     if (st != DIT_OK) return st;
   }
-  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, S, D, c.ln_eps, hmod, hmod + D, m->buf<void>(p.y), s));
+  DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, R, D, c.ln_eps, hmod, hmod + D, m->buf<void>(p.y), s));
   {
-    GemmArgs a = gemm(m->buf<void>(p.y), D, m->g.out_w, D, S, P, D, m->g.out_b);
+    GemmArgs a = gemm(m->buf<void>(p.y), D, m->g.out_w, D, R, P, D, m->g.out_b);
     a.out = u;
     a.ldo = P;
     DIT_RUN(m, PK_GEMM_OUT, s, launch_gemm(m->dt, EPI_STORE_F32, a, s));
   }
-  DIT_RUN(m, PK_EULER, s, launch_unpatchify_euler(u, X, v_out, sigma_next - sigma, c.in_channels, c.lat_f,
-                                  c.lat_h, c.lat_w, c.patch_f, c.patch_h, c.patch_w, s));
+  DIT_RUN(m, PK_EULER, s, launch_unpatchify_euler(u, nb > 1 ? u + (size_t)S * P : nullptr, g, X, v_out,
+                                  sigma_next - sigma, c.in_channels, c.lat_f, c.lat_h, c.lat_w,
+                                  c.patch_f, c.patch_h, c.patch_w, s));
   return DIT_OK;
+}
+
+dit_status check_step(dit_model *m, float *X, int32_t ctx_len, float t, float sigma,
+                      float sigma_next, float *v_out) {
+  if (!m || !ok_ptr(X)) return DIT_ERR_INVALID_ARG;
+  if (v_out && !aligned16(v_out)) return DIT_ERR_INVALID_ARG;
+  if (!std::isfinite(t) || !std::isfinite(sigma) || !std::isfinite(sigma_next))
+    return DIT_ERR_INVALID_ARG;
+  if (ctx_len < 1 || ctx_len > m->cfg.ctx_len_max) return DIT_ERR_SHAPE;
+  return DIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dit_status dit_denoise_step(dit_model *m, float *X, const void *ctx, int32_t ctx_len, float t,
+                            float sigma, float sigma_next, float *v_out, void *stream) {
+  dit_status st = check_step(m, X, ctx_len, t, sigma, sigma_next, v_out);
+  if (st != DIT_OK) return st;
+  if (!ok_ptr(ctx)) return DIT_ERR_INVALID_ARG;
+  const void *ctxs[1] = {ctx};
+  return run_step(m, X, ctxs, 1, ctx_len, t, sigma, sigma_next, 1.0f, v_out,
+                  static_cast<hipStream_t>(stream));
+}
+
+dit_status dit_denoise_step_cfg(dit_model *m, float *X, const void *ctx, const void *ctx_neg,
+                                int32_t ctx_len, float t, float sigma, float sigma_next,
+                                float guidance_scale, float *v_out, void *stream) {
+  dit_status st = check_step(m, X, ctx_len, t, sigma, sigma_next, v_out);
+  if (st != DIT_OK) return st;
+  if (!ok_ptr(ctx) || !ok_ptr(ctx_neg) || !std::isfinite(guidance_scale))
+    return DIT_ERR_INVALID_ARG;
+  if (!m->cfg.guidance) return DIT_ERR_WORKSPACE;
+  const void *ctxs[2] = {ctx, ctx_neg};
+  return run_step(m, X, ctxs, 2, ctx_len, t, sigma, sigma_next, guidance_scale, v_out,
+                  static_cast<hipStream_t>(stream));
 }
 
 dit_status dit_euler_step(float *X, const float *v, int64_t n, float sigma, float sigma_next,

@@ -28,6 +28,18 @@
 namespace dit {
 
 constexpr int ATT_BQ = 128;  // queries per workgroup (4 waves x 32)
+
+// Problem blockIdx.z of a batched launch: its operands start at the batch
+// strides (elements of size es) from the first problem's.
+__device__ __forceinline__ void att_select_batch(AttnArgs &p, int es) {
+  if (p.batch > 1) {
+    const int64_t z = blockIdx.z;
+    p.q = static_cast<const char *>(p.q) + z * p.bq * es;
+    p.k = static_cast<const char *>(p.k) + z * p.bk * es;
+    p.vt = static_cast<const char *>(p.vt) + z * p.bvt * es;
+    p.o = static_cast<char *>(p.o) + z * p.bo * es;
+  }
+}
 constexpr int ATT_BK = 64;   // keys per tile
 
 template <typename T>
@@ -59,6 +71,7 @@ __device__ __forceinline__ void load4_into(typename Frag<T>::type &f, int s, con
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
+  att_select_batch(p, sizeof(T));
   typedef typename Frag<T>::type F;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KROW = HD + VEC;          // K tile row stride (16-byte pad)
@@ -340,6 +353,7 @@ __device__ __forceinline__ void att_exp_half(const f32x16 &x, bf16x8 &lo, bf16x8
 
 template <int HD, int NW>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kernel(AttnArgs p) {
+  att_select_batch(p, 2);
   typedef bf16x8 F;
   constexpr int KROWB = HD * 2;            // bytes per K row
   constexpr int KCHUNK = KROWB / 16;       // 16-byte chunks per K row
@@ -644,8 +658,9 @@ static hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
   // A K tile must give every thread of the workgroup at least one 16-byte piece.
   constexpr int MAXNW = HD >= 64 ? 8 : 4;
   int nw = MAXNW == 8 && a.sk >= 4096 ? 8 : 4;
-  while (nw > 1 && (int64_t)((a.sq + 32 * nw - 1) / (32 * nw)) * a.heads < 128) nw >>= 1;
-  dim3 grid((a.sq + 32 * nw - 1) / (32 * nw), a.heads);
+  const int64_t problems = (int64_t)a.heads * (a.batch > 1 ? a.batch : 1);
+  while (nw > 1 && (int64_t)((a.sq + 32 * nw - 1) / (32 * nw)) * problems < 128) nw >>= 1;
+  dim3 grid((a.sq + 32 * nw - 1) / (32 * nw), a.heads, a.batch > 1 ? a.batch : 1);
   if constexpr (MAXNW == 8) {
     if (nw == 8) {
       attention_bf16_kernel<HD, 8><<<grid, 512, 0, s>>>(a);
@@ -663,7 +678,7 @@ static hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
 
 template <typename T>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
-  dim3 grid((a.sq + ATT_BQ - 1) / ATT_BQ, a.heads);
+  dim3 grid((a.sq + ATT_BQ - 1) / ATT_BQ, a.heads, a.batch > 1 ? a.batch : 1);
   switch (a.head_dim) {
     case 32: attention_kernel<T, 32><<<grid, 256, 0, s>>>(a); break;
     case 64: attention_kernel<T, 64><<<grid, 256, 0, s>>>(a); break;

@@ -152,7 +152,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
         const int c = u >> 2, rr = (u & 3) * 8;
         const int row = rowbase + rr;
         if (row >= M) continue;  // runs past M stay inside the padded rows
-        T *o = static_cast<T *>(dst) + (int64_t)(segc + c) * ld + row;
+        // stacked sequences: token row % seg_rows of sequence row / seg_rows
+        // (a run of 8 never straddles two: seg_rows is a multiple of 8)
+        const int64_t tcol = p.seg_rows > 0
+                                 ? (int64_t)(row / p.seg_rows) * p.seg_bstride + row % p.seg_rows
+                                 : row;
+        T *o = static_cast<T *>(dst) + (int64_t)(segc + c) * ld + tcol;
         const T *srcp = stripT + c * TROW + rr;
         if constexpr (sizeof(T) == 2) {
           *reinterpret_cast<U128 *>(o) = *reinterpret_cast<const U128 *>(srcp);
@@ -186,7 +191,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
           } else if (rope) {
             // pairs (2j, 2j+1) of the head; table column = channel / 2
             const int ch0 = (segc + c8) % (2 * p.rope_half_d);
-            const int64_t t = (int64_t)row * p.rope_half_d + ch0 / 2;
+            const int trow = p.seg_rows > 0 ? row % p.seg_rows : row;  // token position
+            const int64_t t = (int64_t)trow * p.rope_half_d + ch0 / 2;
             pre[it][0] = *reinterpret_cast<const f32x4 *>(p.rope_cos + t);
             pre[it][1] = *reinterpret_cast<const f32x4 *>(p.rope_sin + t);
           }

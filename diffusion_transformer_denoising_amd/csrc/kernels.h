@@ -39,6 +39,13 @@ struct GemmArgs {
   int seg_rope[3];    // rotate (2j, 2j+1) column pairs of this segment
   const float *rope_cos, *rope_sin;  // [M, rope_half_d] tables, per head
   int rope_half_d;
+  // Several sequences stacked along M (the two branches of a guided step):
+  // with seg_rows > 0, row r is token r % seg_rows of sequence r / seg_rows;
+  // its RoPE table row is r % seg_rows, and a transposed segment stores it at
+  // column (r / seg_rows) * seg_bstride + r % seg_rows (seg_rows a multiple
+  // of 8).  seg_rows = 0: one sequence, row r at column r.
+  int seg_rows;
+  int64_t seg_bstride;
   // Grouped launch: `groups` independent problems with the same A and shape;
   // group g uses W = gw[g] and bias = gbias[g] (device tables) and writes split
   // segment s at seg_ptr[s] + g * seg_gstride[s] elements.  groups <= 1: none.
@@ -67,6 +74,10 @@ struct AttnArgs {
   int64_t ldo;
   int sq, sk, heads, head_dim;
   float scale_log2;  // log2(e) / sqrt(head_dim)
+  // batch > 1: independent problems on grid.z, problem z at q + z * bq, k +
+  // z * bk, vt + z * bvt and o + z * bo (elements); batch <= 1: one problem
+  int batch;
+  int64_t bq, bk, bvt, bo;
 };
 hipError_t launch_attention(DType dt, const AttnArgs &a, hipStream_t s);
 
@@ -82,9 +93,12 @@ hipError_t launch_rope_tables(float *cos_t, float *sin_t, int gf, int gh, int gw
 hipError_t launch_patchify(DType dt, const float *X, void *patches, int C, int F, int H, int W,
                            int pf, int ph, int pw, hipStream_t s);
 
-// X += dt * unpatchify(u)  (u float [S, P]); v_out (nullable) = unpatchify(u).
-hipError_t launch_unpatchify_euler(const float *u, float *X, float *v_out, float dt, int C, int F,
-                                   int H, int W, int pf, int ph, int pw, hipStream_t s);
+// X += dt * unpatchify(v), v_out (nullable) = unpatchify(v), with the velocity
+// tokens v = u (float [S, P]) or, when u_neg is given, the guided
+// v = u_neg + g * (u - u_neg).
+hipError_t launch_unpatchify_euler(const float *u, const float *u_neg, float g, float *X,
+                                   float *v_out, float dt, int C, int F, int H, int W, int pf,
+                                   int ph, int pw, hipStream_t s);
 
 // X[i] += dt * v[i], i < n.
 hipError_t launch_euler(float *X, const float *v, int64_t n, float dt, hipStream_t s);

@@ -175,10 +175,15 @@ hipError_t launch_patchify(DType dt, const float *X, void *patches, int C, int F
 // ---------------------------------------------------------------------------
 // Fused unpatchify + Euler: one thread per latent element (c, f, h, w), which
 // reads its velocity from token/element of the patch layout, updates X in
-// place and optionally writes the velocity in latent layout.
+// place and optionally writes the velocity in latent layout.  With guidance
+// the velocity is combined from the two branches' tokens first
+// (v_neg + g (v_pos - v_neg); page "Support New Diffusion Models - SGLang
+// Documentation", sections 1 and 2: guidance_scale, positive and negative
+// condition kwargs).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void unpatchify_euler_kernel(const float *__restrict__ u,
-                                                               float *__restrict__ X,
+                                                               const float *__restrict__ u_neg,
+                                                               float g, float *__restrict__ X,
                                                                float *__restrict__ v_out,
                                                                float dt, int C, int F, int H,
                                                                int W, int pf, int ph, int pw) {
@@ -193,17 +198,22 @@ __global__ __launch_bounds__(256) void unpatchify_euler_kernel(const float *__re
   const int P = C * pf * ph * pw;
   const int64_t n = ((int64_t)(f / pf) * gh + h / ph) * gw + w / pw;
   const int e = ((c * pf + f % pf) * ph + h % ph) * pw + w % pw;
-  const float v = u[n * P + e];
+  float v = u[n * P + e];
+  if (u_neg) {
+    const float vn = u_neg[n * P + e];
+    v = vn + g * (v - vn);
+  }
   X[idx] = X[idx] + dt * v;
   if (v_out) v_out[idx] = v;
 }
 
-hipError_t launch_unpatchify_euler(const float *u, float *X, float *v_out, float dt, int C, int F,
-                                   int H, int W, int pf, int ph, int pw, hipStream_t s) {
+hipError_t launch_unpatchify_euler(const float *u, const float *u_neg, float g, float *X,
+                                   float *v_out, float dt, int C, int F, int H, int W, int pf,
+                                   int ph, int pw, hipStream_t s) {
   const int64_t total = (int64_t)C * F * H * W;
   if (total <= 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
-  unpatchify_euler_kernel<<<grid, 256, 0, s>>>(u, X, v_out, dt, C, F, H, W, pf, ph, pw);
+  unpatchify_euler_kernel<<<grid, 256, 0, s>>>(u, u_neg, g, X, v_out, dt, C, F, H, W, pf, ph, pw);
   return hipGetLastError();
 }
 

@@ -65,10 +65,11 @@ def gemm(dtype: str, epilogue: int, A, W, bias, out, gate=None, tile: int = 0, s
 
 
 class DeviceDiT:
-    def __init__(self, cfg, params: dict, device: str = "cuda", stream: int | None = None):
+    def __init__(self, cfg, params: dict, device: str = "cuda", stream: int | None = None,
+                 guidance: bool = False):
         self.cfg = cfg
         self.device = torch.device(device)
-        self.c = B.make_config(cfg)
+        self.c = B.make_config(cfg, guidance)
         g = params["global"]
         self._keep = []
 
@@ -121,6 +122,22 @@ class DeviceDiT:
         B.dit_denoise_step(self.handle, X.data_ptr(), ctx.data_ptr(), ctx.shape[0], t, sigma,
                            sigma_next, v_out.data_ptr() if v_out is not None else None,
                            self._stream(stream))
+
+    def denoise_step_cfg(self, X: torch.Tensor, ctx: torch.Tensor, ctx_neg: torch.Tensor,
+                         t: float, sigma: float, sigma_next: float, guidance_scale: float,
+                         v_out: torch.Tensor | None = None, stream=None):
+        """Guided step (the model must be built with guidance=True)."""
+        self._check(X, torch.float32)
+        self._check(ctx, torch_dtype(self.cfg))
+        self._check(ctx_neg, torch_dtype(self.cfg))
+        if ctx_neg.shape != ctx.shape:
+            raise ValueError("positive and negative contexts must have the same shape")
+        if v_out is not None:
+            self._check(v_out, torch.float32)
+        B.dit_denoise_step_cfg(self.handle, X.data_ptr(), ctx.data_ptr(), ctx_neg.data_ptr(),
+                               ctx.shape[0], t, sigma, sigma_next, guidance_scale,
+                               v_out.data_ptr() if v_out is not None else None,
+                               self._stream(stream))
 
     def block_forward(self, block: int, x: torch.Tensor, ctx: torch.Tensor, mod: torch.Tensor,
                       stream=None):

@@ -80,6 +80,9 @@ typedef struct {
   float rope_theta;     /* rotary base (10000)                               */
   float ln_eps;         /* LayerNorm epsilon (1e-6)                          */
   int32_t dtype;        /* dit_dtype                                          */
+  int32_t guidance;     /* 1: size the workspace for guided steps
+                           (dit_denoise_step_cfg, two sequences; needs the
+                           token count S a multiple of 8); 0: unguided only  */
 } dit_config;
 
 /* Model-wide parameters (device pointers, element type T).  Shapes:
@@ -157,6 +160,22 @@ dit_status dit_block_forward(dit_model *model, int32_t block, float *x, const vo
  * 1 <= ctx_len <= ctx_len_max. */
 dit_status dit_denoise_step(dit_model *model, float *X, const void *ctx, int32_t ctx_len,
                             float t, float sigma, float sigma_next, float *v_out, void *stream);
+
+/* One denoising step with classifier-free guidance: the network runs on the
+ * same latents and timestep once with the positive context ctx and once with
+ * the negative context ctx_neg (both device T [ctx_len, text_dim]), as one
+ * batch of two sequences that reads every weight once; the guided velocity
+ * V = V_neg + guidance_scale * (V_pos - V_neg) then drives the same Euler
+ * update, X += (sigma_next - sigma) * V, and goes to v_out when given.
+ * ("Support New Diffusion Models - SGLang Documentation", section 1
+ * "Sampling Params": guidance_scale; section 2 "Pipeline Config": the positive
+ * and negative condition kwargs; section 4: negative_prompt_embeds.  The
+ * combination is the conventional one; the pages print no formula.)
+ * The handle must have been created with guidance = 1 (else
+ * DIT_ERR_WORKSPACE); other arguments as for dit_denoise_step. */
+dit_status dit_denoise_step_cfg(dit_model *model, float *X, const void *ctx, const void *ctx_neg,
+                                int32_t ctx_len, float t, float sigma, float sigma_next,
+                                float guidance_scale, float *v_out, void *stream);
 
 /* Flow Euler update X[i] += (sigma_next - sigma) * v[i] for i < n on device
  * float arrays (layout-agnostic).  n == 0 is a no-op. */

@@ -116,3 +116,26 @@ def test_calls_reject_null_handle_and_bad_sizes():
     assert L.dit_euler_step(4098, 4096, 8, 1.0, 0.0, None) == B.DIT_ERR_INVALID_ARG
     assert L.dit_euler_step(4096, 4096, 8, float("nan"), 0.0, None) == B.DIT_ERR_INVALID_ARG
     assert L.dit_destroy(None) == B.DIT_OK
+
+
+def test_guided_workspace_and_validation():
+    # Guided steps stack two sequences: the workspace grows, the flag takes only
+    # 0 / 1, and a token count that is not a multiple of 8 is refused (the
+    # transposed values are stored in runs of 8 rows).
+    for cfg in CONFIGS.values():
+        one = B.dit_workspace_size(B.make_config(cfg))
+        two = B.dit_workspace_size(B.make_config(cfg, guidance=True))
+        assert two > one
+    c = B.make_config(CONFIGS["image_s_bf16"], guidance=True)
+    c.guidance = 2
+    with pytest.raises(B.DitError) as e:
+        B.dit_workspace_size(c)
+    assert e.value.status == B.DIT_ERR_INVALID_ARG
+    odd = CONFIGS["image_s_bf16"].with_(latent=(1, 6, 6))   # S = 9 tokens
+    assert B.dit_workspace_size(B.make_config(odd)) > 0
+    with pytest.raises(B.DitError) as e:
+        B.dit_workspace_size(B.make_config(odd, guidance=True))
+    assert e.value.status == B.DIT_ERR_UNSUPPORTED
+    L = B.lib()
+    assert L.dit_denoise_step_cfg(None, 4096, 4096, 4096, 1, 1.0, 1.0, 0.0, 4.0, None,
+                                  None) == B.DIT_ERR_INVALID_ARG

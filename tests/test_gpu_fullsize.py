@@ -138,3 +138,45 @@ def test_denoise_step_one_block_full_size():
     X0tok = oracle.patchify(X0, cfg.patch)[rows]
     ref = oracle.euler_step(X0tok, u, sig[3], sig[4])
     assert rel_l2(Xtok, ref) < tolerances(cfg)["latents"]
+
+
+def test_guided_step_one_block_full_size():
+    """The guided step at the Wan-1.3B shape with one block (32760 tokens: the
+    transposed values of the two stacked sequences at a padded column stride):
+    the guided velocity and latents at sampled tokens against the oracle's two
+    branches combined with g = 4.  The cross-attention output projection is
+    scaled up so that the branches differ visibly."""
+    require_gpu()
+    cfg = workload("wan1p3b_bf16", num_blocks=1)
+    announce("guided step full wan1p3b 1 block")
+    prm = SP.make_params(cfg)
+    prm["blocks"][0]["co_w"] = storage_round(prm["blocks"][0]["co_w"] * 25.0, cfg.dtype)
+    m = DeviceDiT(cfg, prm, guidance=True)
+    X0 = SP.make_latents(cfg)
+    E = SP.make_ctx(cfg)
+    En = SP.make_ctx(cfg, seed=3)
+    sig = oracle.flow_sigmas(cfg.steps, cfg.shift)
+    t = float(np.float32(1000.0 * sig[3]))
+    X = torch.from_numpy(X0).cuda()
+    v = torch.empty_like(X)
+    m.denoise_step_cfg(X, dev_tensor(E, cfg.dtype), dev_tensor(En, cfg.dtype), t, float(sig[3]),
+                       float(sig[4]), 4.0, v_out=v)
+    torch.cuda.synchronize()
+    g = prm["global"]
+    temb, e = oracle.time_embedding(t, g, cfg.freq_dim)
+    x = oracle.linear(oracle.patchify(X0, cfg.patch), g["pe_w"], g["pe_b"])
+    rows = _rows(cfg.tokens, 16, 29)
+    mod = oracle.block_modulation(e, prm["blocks"][0]["table"])
+    pos = oracle.token_positions(cfg.grid)
+    u = {}
+    for name, ctx in (("pos", E), ("neg", En)):
+        c = oracle.context_projection(ctx, g, cfg)
+        xr = oracle.dit_block(x, c, mod, prm["blocks"][0], cfg, pos, rows=rows)
+        u[name] = oracle.final_layer(xr, temb, g, cfg)
+    assert rel_l2(u["pos"] - u["neg"], u["neg"]) > 0.05
+    ug = u["neg"] + 4.0 * (u["pos"] - u["neg"])
+    vtok = oracle.patchify(to_np(v), cfg.patch)[rows]
+    assert rel_l2(vtok, ug) < tolerances(cfg)["velocity"]
+    Xtok = oracle.patchify(to_np(X), cfg.patch)[rows]
+    ref = oracle.euler_step(oracle.patchify(X0, cfg.patch)[rows], ug, sig[3], sig[4])
+    assert rel_l2(Xtok, ref) < tolerances(cfg)["latents"]
