@@ -1,7 +1,7 @@
 """Benchmark: denoise steps per second of one DiT denoising step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--guidance G] [--no-cpu-baseline] [--calibrate-copy]
+                    [--guidance G] [--offload] [--no-cpu-baseline] [--calibrate-copy]
 
 A step is one call of dit_denoise_step: time embedding, context projection,
 patch embedding, every DiT block (LayerNorm+adaLN, QKV projection, RoPE,
@@ -10,7 +10,10 @@ head, then the fused unpatchify + Euler update.  Inputs and weights are seeded
 synthetic data already resident in HBM when timing starts; the timestep and
 sigmas cycle through the workload's flow schedule.  With --guidance G a step is
 one call of dit_denoise_step_cfg instead: both branches (positive context and
-a second, negative one) as one batch of two sequences, guidance scale G.
+a second, negative one) as one batch of two sequences, guidance scale G.  With
+--offload the block weights live in page-locked host memory and every step
+streams them block by block into two HBM slots (layerwise offload); the line
+then also reports the streamed bytes per step and their rate.
 
 Prints ONE JSON line on stdout (diagnostics go to stderr):
   value          whole-job steps/s (K timed steps, bracketed by
@@ -145,6 +148,8 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--guidance", type=float, default=None,
                     help="time the guided step (classifier-free guidance) at this scale")
+    ap.add_argument("--offload", action="store_true",
+                    help="layerwise offload: block weights streamed from pinned host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (the known-size kernel "
@@ -183,7 +188,7 @@ def main(argv=None) -> int:
     guided = args.guidance is not None
     nb = 2 if guided else 1
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-    m = DeviceDiT(cfg, prm, guidance=guided)
+    m = DeviceDiT(cfg, prm, guidance=guided, offload=args.offload)
     X = torch.from_numpy(X0).cuda()
     Ed = torch.from_numpy(E).cuda().to(torch_dtype(cfg))
     # the negative context of a guided step: its own seed (3)
@@ -298,7 +303,9 @@ def main(argv=None) -> int:
                    "text_dim": cfg.text_dim, "latent": list(cfg.latent_shape),
                    "schedule_steps": cfg.steps, "shift": cfg.shift, "batch": 1,
                    "parallelism": "single GPU",
-                   **({"guidance_scale": args.guidance, "sequences": 2} if guided else {})},
+                   **({"guidance_scale": args.guidance, "sequences": 2} if guided else {}),
+                   **({"weights": "layerwise offload from pinned host memory"}
+                      if args.offload else {})},
         "step_tflops": round(fl["total"] / (ms_per_step / 1e3) / 1e12, 2),
         "step_frac_of_peak": round(fl["total"] / (ms_per_step / 1e3) / 1e12 / peak, 4),
         "attention": {"tflops": round(att_tf, 2), "frac_of_peak": round(att_tf / peak, 4)},
@@ -306,6 +313,14 @@ def main(argv=None) -> int:
         "roofline": roof,
         "kernels": kernels,
     }
+    if args.offload:
+        es = 2 if cfg.dtype == "bf16" else 4
+        D, F = cfg.hidden, cfg.mlp_hidden
+        streamed = es * cfg.num_blocks * (8 * D * D + 2 * F * D + 9 * D + F)
+        out["offload"] = {"bytes_per_step": streamed,
+                          "host_to_device_gbs": round(streamed / (ms_per_step / 1e3) / 1e9, 2)}
+        log(f"[bench] offload: {streamed / 1e9:.3f} GB streamed per step, "
+            f"{out['offload']['host_to_device_gbs']} GB/s")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         out["cpu_baseline"] = (cpu_baseline(cfg, prm, X0, E, E_neg=SP.make_ctx(cfg, seed=3),

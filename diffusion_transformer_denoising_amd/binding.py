@@ -34,7 +34,7 @@ class dit_config(ctypes.Structure):
         "num_blocks", "hidden", "heads", "head_dim", "mlp_hidden", "freq_dim", "in_channels",
         "patch_f", "patch_h", "patch_w", "lat_f", "lat_h", "lat_w", "rope_f", "rope_h", "rope_w",
         "ctx_len_max", "text_dim")] + [("rope_theta", c_f32), ("ln_eps", c_f32), ("dtype", c_i32),
-                                       ("guidance", c_i32)]
+                                       ("guidance", c_i32), ("offload", c_i32)]
 
 
 GLOBAL_FIELDS = ("t1_w", "t1_b", "t2_w", "t2_b", "mod_w", "mod_b", "txt_w", "txt_b",
@@ -125,13 +125,15 @@ def dit_status_string(status: int) -> str:
     return status_string(status)
 
 
-def make_config(cfg, guidance: bool = False) -> dit_config:
+def make_config(cfg, guidance: bool = False, offload: bool = False) -> dit_config:
     """dit_config from any object with the workload attributes (hidden, heads,
     head_dim, mlp_hidden, num_blocks, in_channels, patch, latent, rope,
     ctx_len, text_dim, freq_dim, rope_theta, ln_eps, dtype); guidance sizes
-    the workspace for guided steps."""
+    the workspace for guided steps; offload streams the block weights from
+    page-locked host memory."""
     c = dit_config()
     c.guidance = 1 if guidance else 0
+    c.offload = 1 if offload else 0
     c.num_blocks, c.hidden, c.heads, c.head_dim = cfg.num_blocks, cfg.hidden, cfg.heads, cfg.head_dim
     c.mlp_hidden, c.freq_dim, c.in_channels = cfg.mlp_hidden, cfg.freq_dim, cfg.in_channels
     c.patch_f, c.patch_h, c.patch_w = cfg.patch

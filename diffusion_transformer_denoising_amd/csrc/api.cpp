@@ -37,8 +37,20 @@ struct Plan {
   // then the two rows of the head table
   size_t cos_t, sin_t, x, y, q, k, vt, o, h, c, kc, vct, patches, u, h1, temb, e, bmod, hmod,
       gtab;
+  // layerwise offload: every block's modulation table stays resident; the
+  // other block weights stream through two slots, field f of a slot at
+  // slot[s] + wofs[f] (fields in dit_block_weights order; table unused)
+  size_t tables, slot[2], wofs[15], wbytes[15];
   size_t total;
 };
+
+// Elements of each dit_block_weights field, in declaration order.
+void block_field_elems(const dit_config &c, int64_t n[15]) {
+  const int64_t D = c.hidden, F = c.mlp_hidden;
+  const int64_t v[15] = {6 * D, 3 * D * D, 3 * D, D * D, D, D * D, D, 2 * D * D, 2 * D,
+                         D * D, D, F * D, F, D * F, D};
+  for (int i = 0; i < 15; ++i) n[i] = v[i];
+}
 
 bool plan_layout(const dit_config &c, Plan &p) {
   p.es = c.dtype == DIT_BF16 ? 2 : 4;
@@ -81,6 +93,20 @@ bool plan_layout(const dit_config &c, Plan &p) {
   p.bmod = take(f4 * 6 * p.D * c.num_blocks);
   p.hmod = take(f4 * 2 * p.D);
   p.gtab = take(sizeof(void *) * (3 * (size_t)c.num_blocks + 2));
+  p.tables = p.slot[0] = p.slot[1] = 0;
+  if (c.offload) {
+    p.tables = take(es * (size_t)c.num_blocks * 6 * p.D);
+    int64_t n[15];
+    block_field_elems(c, n);
+    size_t sb = 0;
+    for (int f = 0; f < 15; ++f) {
+      p.wbytes[f] = es * (size_t)n[f];
+      p.wofs[f] = sb;
+      if (f > 0) sb = round_up(sb + p.wbytes[f], WS_ALIGN);  // field 0 (table) stays resident
+    }
+    p.slot[0] = take(sb);
+    p.slot[1] = take(sb);
+  }
   p.total = off;
   return true;
 }
@@ -110,6 +136,7 @@ dit_status check_config(const dit_config *c) {
                     (c->lat_w / c->patch_w);
   if (S > (int64_t)1 << 30) return DIT_ERR_UNSUPPORTED;
   if (c->guidance != 0 && c->guidance != 1) return DIT_ERR_INVALID_ARG;
+  if (c->offload != 0 && c->offload != 1) return DIT_ERR_INVALID_ARG;
   // guided steps stack two sequences; the transposed values are written in
   // runs of 8 rows, which must not straddle them
   if (c->guidance && S % 8) return DIT_ERR_UNSUPPORTED;
@@ -187,11 +214,22 @@ struct dit_model {
   dit_config cfg;
   DType dt;
   dit_global_weights g;
-  std::vector<dit_block_weights> blocks;
+  std::vector<dit_block_weights> blocks;  // device pointers, or host ones with offload
   char *ws;
   Plan plan;
   Profiler prof;
+  // layerwise offload: block copies run on their own stream; ready[s] marks
+  // slot s filled, freed[s] the end of the last block that read it
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ready[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
   template <typename U> U *buf(size_t off) const { return reinterpret_cast<U *>(ws + off); }
+  ~dit_model() {
+    for (int i = 0; i < 2; ++i) {
+      if (ready[i]) (void)hipEventDestroy(ready[i]);
+      if (freed[i]) (void)hipEventDestroy(freed[i]);
+    }
+    if (copy_stream) (void)hipStreamDestroy(copy_stream);
+  }
 };
 
 namespace {
@@ -227,15 +265,15 @@ GemmArgs gemm(const void *A, int64_t lda, const void *W, int64_t ldw, int M, int
   return a;
 }
 
-// One block on the residual stream x [nb S, D] (nb stacked sequences sharing
-// the modulation) with projected context ctx [L, D] (one sequence, computed
-// here) or, with ckv_ready, the cross K / V^T of context n already in slot n
-// of kc / vct.
-dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, const float *mod,
-                     hipStream_t s, bool ckv_ready, int nb) {
+// One block (weights w, device pointers) on the residual stream x [nb S, D]
+// (nb stacked sequences sharing the modulation) with the projected contexts
+// ctx[n] [L, D], whose cross K / V^T this block computes into slot n of kc /
+// vct, or, with ckv_ready, finds there already.
+dit_status run_block(dit_model *m, const dit_block_weights &w, int b, float *x,
+                     const void *const *ctx, int L, const float *mod, hipStream_t s,
+                     bool ckv_ready, int nb) {
   const dit_config &c = m->cfg;
   const Plan &p = m->plan;
-  const dit_block_weights &w = m->blocks[b];
   const int S = (int)p.S, D = (int)p.D, F = (int)p.F, R = nb * S;
   const int B = c.num_blocks;
   void *y = m->buf<void>(p.y), *q = m->buf<void>(p.q), *k = m->buf<void>(p.k);
@@ -284,11 +322,13 @@ dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, cons
     a.out = q; a.ldo = D;
     DIT_RUN(m, PK_GEMM_CQ, s, launch_gemm(m->dt, EPI_STORE, a, s));
   }
-  if (!ckv_ready) {
-    GemmArgs a = gemm(ctx, D, w.ckv_w, D, L, 2 * D, D, w.ckv_b);
+  for (int n = 0; n < nb && !ckv_ready; ++n) {
+    GemmArgs a = gemm(ctx[n], D, w.ckv_w, D, L, 2 * D, D, w.ckv_b);
     a.seg_width = D;
-    a.seg_ptr[0] = kc; a.seg_ld[0] = D; a.seg_trans[0] = 0;
-    a.seg_ptr[1] = vct; a.seg_ld[1] = p.L_pad; a.seg_trans[1] = 1;
+    a.seg_ptr[0] = static_cast<char *>(kc) + p.es * n * ctx_k;
+    a.seg_ld[0] = D; a.seg_trans[0] = 0;
+    a.seg_ptr[1] = static_cast<char *>(vct) + p.es * n * ctx_v;
+    a.seg_ld[1] = p.L_pad; a.seg_trans[1] = 1;
     DIT_RUN(m, PK_GEMM_CKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
   }
   {
@@ -317,6 +357,38 @@ dit_status run_block(dit_model *m, int b, float *x, const void *ctx, int L, cons
     DIT_RUN(m, PK_GEMM_MLP2, s, launch_gemm(m->dt, EPI_RESIDUAL, a, s));
   }
   return DIT_OK;
+}
+
+// Device view of block b's weights in offload slot `slot` (its modulation
+// table from the resident copy).
+dit_block_weights slot_weights(const dit_model *m, int slot, int b) {
+  const Plan &p = m->plan;
+  const void **f = nullptr;
+  dit_block_weights w{};
+  f = reinterpret_cast<const void **>(&w);
+  char *base = m->ws + p.slot[slot];
+  for (int i = 1; i < 15; ++i) f[i] = base + p.wofs[i];
+  f[0] = m->ws + p.tables + p.es * (size_t)b * 6 * p.D;
+  return w;
+}
+
+// Block b's weights (pinned host memory) into slot `slot` on stream cs; the
+// caller orders cs after the slot's previous reader.  Fields that sit in host
+// memory exactly as in the slot (each at the previous one's offset plus the
+// distance between their slot offsets) go over in one transfer.
+hipError_t copy_block(const dit_model *m, int b, int slot, hipStream_t cs) {
+  const Plan &p = m->plan;
+  const char *const *src = reinterpret_cast<const char *const *>(&m->blocks[b]);
+  char *base = m->ws + p.slot[slot];
+  for (int i = 1; i < 15;) {
+    int j = i + 1;
+    while (j < 15 && src[j] == src[i] + (p.wofs[j] - p.wofs[i])) ++j;
+    const size_t n = p.wofs[j - 1] + p.wbytes[j - 1] - p.wofs[i];
+    hipError_t e = hipMemcpyAsync(base + p.wofs[i], src[i], n, hipMemcpyHostToDevice, cs);
+    if (e != hipSuccess) return e;
+    i = j;
+  }
+  return hipSuccess;
 }
 
 dit_status run_time_path(dit_model *m, float t, float *bmod, float *hmod, float *temb,
@@ -382,15 +454,29 @@ dit_status dit_create(const dit_config *cfg, const dit_weights *weights, void *w
   const int B = cfg->num_blocks;
   std::vector<const void *> tab(3 * (size_t)B + 2);
   for (int b = 0; b < B; ++b) {
-    tab[b] = weights->blocks[b].ckv_w;
-    tab[B + b] = weights->blocks[b].ckv_b;
-    tab[2 * B + b] = weights->blocks[b].table;
+    // with offload the block weights are host pointers: no grouped cross K/V,
+    // and the modulation tables are read from their resident copies
+    tab[b] = cfg->offload ? nullptr : weights->blocks[b].ckv_w;
+    tab[B + b] = cfg->offload ? nullptr : weights->blocks[b].ckv_b;
+    tab[2 * B + b] = cfg->offload ? m->ws + p.tables + p.es * (size_t)b * 6 * cfg->hidden
+                                  : weights->blocks[b].table;
   }
   const size_t es = cfg->dtype == DIT_BF16 ? 2 : 4;
   tab[3 * B] = weights->global.head_table;
   tab[3 * B + 1] = static_cast<const char *>(weights->global.head_table) + es * cfg->hidden;
   hipError_t e = hipMemcpyAsync(m->ws + p.gtab, tab.data(), tab.size() * sizeof(void *),
                                 hipMemcpyHostToDevice, s);
+  if (cfg->offload) {
+    for (int b = 0; b < B && e == hipSuccess; ++b)
+      e = hipMemcpyAsync(m->ws + p.tables + p.es * (size_t)b * 6 * cfg->hidden,
+                         weights->blocks[b].table, p.es * 6 * (size_t)cfg->hidden,
+                         hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->copy_stream, hipStreamNonBlocking);
+    for (int i = 0; i < 2 && e == hipSuccess; ++i) {
+      e = hipEventCreateWithFlags(&m->ready[i], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&m->freed[i], hipEventDisableTiming);
+    }
+  }
   if (e == hipSuccess) e = hipStreamSynchronize(s);  // `tab` is released on return
   if (e == hipSuccess)
     e = launch_rope_tables(m->buf<float>(p.cos_t), m->buf<float>(p.sin_t),
@@ -415,7 +501,12 @@ dit_status dit_block_forward(dit_model *m, int32_t block, float *x, const void *
   if (!m || !ok_ptr(x) || !ok_ptr(ctx) || !ok_ptr(mod)) return DIT_ERR_INVALID_ARG;
   if (block < 0 || block >= m->cfg.num_blocks) return DIT_ERR_SHAPE;
   if (ctx_len < 1 || ctx_len > m->cfg.ctx_len_max) return DIT_ERR_SHAPE;
-  return run_block(m, block, x, ctx, ctx_len, mod, static_cast<hipStream_t>(stream), false, 1);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void *ctxs[1] = {ctx};
+  if (!m->cfg.offload) return run_block(m, m->blocks[block], block, x, ctxs, ctx_len, mod, s, false, 1);
+  // offload: the block's weights into slot 0 on the call's own stream first
+  DIT_TRY(copy_block(m, block, 0, s));
+  return run_block(m, slot_weights(m, 0, block), block, x, ctxs, ctx_len, mod, s, false, 1);
 }
 
 }  // extern "C"
@@ -463,8 +554,9 @@ dit_status run_step(dit_model *m, float *X, const void *const *ctx, int nb, int 
     DIT_TRY(hipMemcpyAsync(x + (size_t)n * S * D, x, sizeof(float) * (size_t)S * D,
                            hipMemcpyDeviceToDevice, s));
   // cross K / V^T of every block in one grouped launch per context: they
-  // depend on the context only, not on the residual stream
-  for (int n = 0; n < nb; ++n) {
+  // depend on the context only, not on the residual stream (with offload each
+  // block computes its own from the streamed weights)
+  for (int n = 0; n < nb && !c.offload; ++n) {
     GemmArgs a = gemm(cproj[n], D, nullptr, D, ctx_len, 2 * D, D, nullptr);
     a.seg_width = D;
     a.seg_ptr[0] = m->buf<char>(p.kc) + p.es * (size_t)n * B * c.ctx_len_max * D;
@@ -478,9 +570,35 @@ dit_status run_step(dit_model *m, float *X, const void *const *ctx, int nb, int 
     a.seg_gstride[1] = (int64_t)D * p.L_pad;
     DIT_RUN(m, PK_GEMM_CKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
   }
-  for (int b = 0; b < B; ++b) {
-    st = run_block(m, b, x, nullptr, ctx_len, bmod + (int64_t)b * 6 * D, s, true, nb);
-    if (st != DIT_OK) return st;
+  if (!c.offload) {
+    for (int b = 0; b < B; ++b) {
+      st = run_block(m, m->blocks[b], b, x, cproj, ctx_len, bmod + (int64_t)b * 6 * D, s, true, nb);
+      if (st != DIT_OK) return st;
+    }
+  } else {
+    // Layerwise offload: block b runs from slot b & 1 while block b + 1 is
+    // copied into the other; block b + 2's copy waits for block b's end.
+    // Both slots are free once the stream reaches this point.
+    hipStream_t cs = m->copy_stream;
+    for (int k = 0; k < 2; ++k) DIT_TRY(hipEventRecord(m->freed[k], s));
+    for (int b = 0; b < B && b < 2; ++b) {
+      DIT_TRY(hipStreamWaitEvent(cs, m->freed[b], 0));
+      DIT_TRY(copy_block(m, b, b, cs));
+      DIT_TRY(hipEventRecord(m->ready[b], cs));
+    }
+    for (int b = 0; b < B; ++b) {
+      const int sl = b & 1;
+      DIT_TRY(hipStreamWaitEvent(s, m->ready[sl], 0));
+      st = run_block(m, slot_weights(m, sl, b), b, x, cproj, ctx_len, bmod + (int64_t)b * 6 * D,
+                     s, false, nb);
+      if (st != DIT_OK) return st;
+      if (b + 2 < B) {
+        DIT_TRY(hipEventRecord(m->freed[sl], s));
+        DIT_TRY(hipStreamWaitEvent(cs, m->freed[sl], 0));
+        DIT_TRY(copy_block(m, b + 2, sl, cs));
+        DIT_TRY(hipEventRecord(m->ready[sl], cs));
+      }
+    }
   }
   DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, R, D, c.ln_eps, hmod, hmod + D, m->buf<void>(p.y), s));
   {

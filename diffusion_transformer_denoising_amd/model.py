@@ -66,10 +66,10 @@ def gemm(dtype: str, epilogue: int, A, W, bias, out, gate=None, tile: int = 0, s
 
 class DeviceDiT:
     def __init__(self, cfg, params: dict, device: str = "cuda", stream: int | None = None,
-                 guidance: bool = False):
+                 guidance: bool = False, offload: bool = False, pack_offload: bool = True):
         self.cfg = cfg
         self.device = torch.device(device)
-        self.c = B.make_config(cfg, guidance)
+        self.c = B.make_config(cfg, guidance, offload)
         g = params["global"]
         self._keep = []
 
@@ -77,6 +77,29 @@ class DeviceDiT:
             t = to_device(a, cfg.dtype, self.device)
             self._keep.append(t)
             return t.data_ptr()
+
+        def pinned(a):
+            t = to_device(a, cfg.dtype, torch.device("cpu")).pin_memory()
+            self._keep.append(t)
+            return t.data_ptr()
+
+        def pinned_block(p):
+            # the weights of one offloaded block in one page-locked buffer, each
+            # field after the table at the first 256-byte boundary past the
+            # previous one (the layout the library copies in one transfer)
+            host = {n: to_device(p[n], cfg.dtype, torch.device("cpu")).reshape(-1).view(torch.uint8)
+                    for n in B.BLOCK_FIELDS}
+            offs, end = {}, 0
+            for n in B.BLOCK_FIELDS[1:]:
+                offs[n] = end
+                end = (end + host[n].numel() + 255) // 256 * 256
+            buf = torch.empty(end, dtype=torch.uint8, pin_memory=True)
+            for n in B.BLOCK_FIELDS[1:]:
+                buf[offs[n]:offs[n] + host[n].numel()].copy_(host[n])
+            table = host[B.BLOCK_FIELDS[0]].clone().pin_memory()
+            self._keep += [buf, table]
+            return {B.BLOCK_FIELDS[0]: table.data_ptr(),
+                    **{n: buf.data_ptr() + offs[n] for n in B.BLOCK_FIELDS[1:]}}
 
         gw = B.dit_global_weights()
         for name in B.GLOBAL_FIELDS:
@@ -86,8 +109,14 @@ class DeviceDiT:
         for i, p in enumerate(params["blocks"]):
             if p is None:
                 raise ValueError(f"block {i} parameters missing")
+            if offload and pack_offload:
+                ptrs = pinned_block(p)
+            elif offload:   # one page-locked buffer per field: copied field by field
+                ptrs = {n: pinned(p[n]) for n in B.BLOCK_FIELDS}
+            else:
+                ptrs = {n: up(p[n]) for n in B.BLOCK_FIELDS}
             for name in B.BLOCK_FIELDS:
-                setattr(self._blocks[i], name, up(p[name]))
+                setattr(self._blocks[i], name, ptrs[name])
         self._w = B.dit_weights()
         self._w.global_ = gw
         self._w.blocks = ctypes.cast(self._blocks, ctypes.POINTER(B.dit_block_weights))

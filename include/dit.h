@@ -83,6 +83,23 @@ typedef struct {
   int32_t guidance;     /* 1: size the workspace for guided steps
                            (dit_denoise_step_cfg, two sequences; needs the
                            token count S a multiple of 8); 0: unguided only  */
+  int32_t offload;      /* 1: layerwise weight offload.  The per-block
+                           weights (dit_block_weights) are then HOST pointers
+                           into page-locked memory (hipHostMalloc or
+                           equivalent); each step streams every block into
+                           one of two workspace slots on an internal copy
+                           stream while the previous block runs ("Support New
+                           Diffusion Models - SGLang Documentation", section
+                           "5. Distributed and memory integration": layerwise
+                           offload over the repeated blocks; section "Verify
+                           the Port": compared with the resident baseline).
+                           The block's modulation table is copied to the
+                           device once, by dit_create.  Fields after it that
+                           lie in one allocation in declaration order, each
+                           at the first 256-byte boundary after the end of
+                           the previous one, are moved in a single transfer;
+                           any other placement is valid but copied field by
+                           field.  0: all weights resident on the device    */
 } dit_config;
 
 /* Model-wide parameters (device pointers, element type T).  Shapes:
@@ -118,7 +135,10 @@ typedef struct {
 typedef struct {
   dit_global_weights global;
   const dit_block_weights *blocks; /* HOST array of num_blocks entries; copied
-                                      by dit_create                           */
+                                      by dit_create.  With offload, the
+                                      weights these entries point to are in
+                                      page-locked host memory and must stay
+                                      there for the handle's lifetime        */
 } dit_weights;
 
 typedef struct dit_model dit_model;

@@ -139,3 +139,24 @@ def test_guided_workspace_and_validation():
     L = B.lib()
     assert L.dit_denoise_step_cfg(None, 4096, 4096, 4096, 1, 1.0, 1.0, 0.0, 4.0, None,
                                   None) == B.DIT_ERR_INVALID_ARG
+
+
+def test_offload_workspace_and_validation():
+    # Layerwise offload keeps every modulation table resident and adds two
+    # slots that each hold one block's other weights; the flag takes 0 / 1.
+    for cfg in CONFIGS.values():
+        es = 2 if cfg.dtype == "bf16" else 4
+        D, F, nb = cfg.hidden, cfg.mlp_hidden, cfg.num_blocks
+        block = 8 * D * D + 2 * F * D + 9 * D + F   # one block, table excluded
+        one = B.dit_workspace_size(B.make_config(cfg))
+        off = B.dit_workspace_size(B.make_config(cfg, offload=True))
+        extra = off - one
+        assert extra >= es * (2 * block + nb * 6 * D)
+        assert extra <= es * (2 * block + nb * 6 * D) + 64 * 1024   # field alignment only
+        both = B.dit_workspace_size(B.make_config(cfg, guidance=True, offload=True))
+        assert both >= B.dit_workspace_size(B.make_config(cfg, guidance=True)) + extra - 64 * 1024
+    c = B.make_config(CONFIGS["image_s_bf16"], offload=True)
+    c.offload = 3
+    with pytest.raises(B.DitError) as e:
+        B.dit_workspace_size(c)
+    assert e.value.status == B.DIT_ERR_INVALID_ARG
