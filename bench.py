@@ -1,7 +1,8 @@
 """Benchmark: denoise steps per second of one DiT denoising step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--guidance G] [--offload] [--no-cpu-baseline] [--calibrate-copy]
+                    [--guidance G] [--offload] [--cache] [--no-cpu-baseline]
+                    [--calibrate-copy]
 
 A step is one call of dit_denoise_step: time embedding, context projection,
 patch embedding, every DiT block (LayerNorm+adaLN, QKV projection, RoPE,
@@ -13,7 +14,11 @@ one call of dit_denoise_step_cfg instead: both branches (positive context and
 a second, negative one) as one batch of two sequences, guidance scale G.  With
 --offload the block weights live in page-locked host memory and every step
 streams them block by block into two HBM slots (layerwise offload); the line
-then also reports the streamed bytes per step and their rate.
+then also reports the streamed bytes per step and their rate.  With --cache the
+steps go through dit_denoise_step_cached with the Cache-DiT knobs of the pages'
+deployment (FN 2, BN 1, WARMUP 4, RDT 0.4, MC 4, TaylorSeer order 2): the timed
+steps are whole sampling runs of the workload's schedule, each begun afresh,
+and the line reports how many steps reused the cache.
 
 Prints ONE JSON line on stdout (diagnostics go to stderr):
   value          whole-job steps/s (K timed steps, bracketed by
@@ -47,6 +52,9 @@ METRIC = "denoise steps/sec per config + attention/GEMM TFLOP/s as % bf16 MFMA p
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "image_s_bf16"
+# Cache-DiT knobs of the pages' GLM-Image denoisers (page "Disaggregated
+# Diffusion Pipeline", section "GLM-Image distributed mode")
+CACHE_KNOBS = dict(fn=2, bn=1, warmup=4, rdt=0.4, max_consecutive=4, taylorseer=True, ts_order=2)
 
 GEMM_KINDS = ("gemm_qkv_rope", "gemm_o", "gemm_cross_q", "gemm_cross_kv", "gemm_cross_o",
               "gemm_mlp1_gelu", "gemm_mlp2", "gemm_text_proj", "gemm_patch_embed", "gemm_head")
@@ -150,6 +158,8 @@ def main(argv=None) -> int:
                     help="time the guided step (classifier-free guidance) at this scale")
     ap.add_argument("--offload", action="store_true",
                     help="layerwise offload: block weights streamed from pinned host memory")
+    ap.add_argument("--cache", action="store_true",
+                    help="block caching across steps with the pages' Cache-DiT knobs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (the known-size kernel "
@@ -188,7 +198,7 @@ def main(argv=None) -> int:
     guided = args.guidance is not None
     nb = 2 if guided else 1
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-    m = DeviceDiT(cfg, prm, guidance=guided, offload=args.offload)
+    m = DeviceDiT(cfg, prm, guidance=guided, offload=args.offload, cache=args.cache)
     X = torch.from_numpy(X0).cuda()
     Ed = torch.from_numpy(E).cuda().to(torch_dtype(cfg))
     # the negative context of a guided step: its own seed (3)
@@ -197,16 +207,26 @@ def main(argv=None) -> int:
     sched = [(float(np.float32(1000.0 * sig[k])), float(sig[k]), float(sig[k + 1]))
              for k in range(cfg.steps)]
 
+    hits = [0]
+
     def run(n, k0=0):
         for i in range(n):
-            t, s0, s1 = sched[(k0 + i) % cfg.steps]
-            if guided:
+            k = (k0 + i) % cfg.steps
+            t, s0, s1 = sched[k]
+            if args.cache:
+                if k == 0:
+                    m.cache_begin(**CACHE_KNOBS)
+                m.denoise_step_cached(X, Ed, t, s0, s1, ctx_neg=End,
+                                      guidance_scale=args.guidance if guided else 1.0)
+                hits[0] += m.cache_state()["hit"]
+            elif guided:
                 m.denoise_step_cfg(X, Ed, End, t, s0, s1, args.guidance)
             else:
                 m.denoise_step(X, Ed, t, s0, s1)
 
     run(args.warmup)
     torch.cuda.synchronize()
+    hits[0] = 0
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -218,6 +238,7 @@ def main(argv=None) -> int:
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1)
     ms_per_step = ms / args.steps
+    timed_hits = hits[0]
     log(f"[bench] {args.steps} steps: {ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
 
     # second pass over the same K steps with every launch bracketed by events
@@ -305,7 +326,8 @@ def main(argv=None) -> int:
                    "parallelism": "single GPU",
                    **({"guidance_scale": args.guidance, "sequences": 2} if guided else {}),
                    **({"weights": "layerwise offload from pinned host memory"}
-                      if args.offload else {})},
+                      if args.offload else {}),
+                   **({"cache": dict(CACHE_KNOBS, runs_of=cfg.steps)} if args.cache else {})},
         "step_tflops": round(fl["total"] / (ms_per_step / 1e3) / 1e12, 2),
         "step_frac_of_peak": round(fl["total"] / (ms_per_step / 1e3) / 1e12 / peak, 4),
         "attention": {"tflops": round(att_tf, 2), "frac_of_peak": round(att_tf / peak, 4)},
@@ -313,6 +335,9 @@ def main(argv=None) -> int:
         "roofline": roof,
         "kernels": kernels,
     }
+    if args.cache:
+        out["cache"] = {"cached_steps": timed_hits, "steps": args.steps}
+        log(f"[bench] cache: {timed_hits} of {args.steps} timed steps reused the cache")
     if args.offload:
         es = 2 if cfg.dtype == "bf16" else 4
         D, F = cfg.hidden, cfg.mlp_hidden

@@ -34,7 +34,17 @@ class dit_config(ctypes.Structure):
         "num_blocks", "hidden", "heads", "head_dim", "mlp_hidden", "freq_dim", "in_channels",
         "patch_f", "patch_h", "patch_w", "lat_f", "lat_h", "lat_w", "rope_f", "rope_h", "rope_w",
         "ctx_len_max", "text_dim")] + [("rope_theta", c_f32), ("ln_eps", c_f32), ("dtype", c_i32),
-                                       ("guidance", c_i32), ("offload", c_i32)]
+                                       ("guidance", c_i32), ("offload", c_i32), ("cache", c_i32)]
+
+
+class dit_cache_params(ctypes.Structure):
+    _fields_ = [("fn", c_i32), ("bn", c_i32), ("warmup", c_i32), ("rdt", c_f32),
+                ("max_consecutive", c_i32), ("taylorseer", c_i32), ("ts_order", c_i32)]
+
+
+class dit_cache_state(ctypes.Structure):
+    _fields_ = [("step", c_i32), ("consecutive", c_i32), ("last_full", c_i32), ("factors", c_i32),
+                ("hit", c_i32), ("cached_total", c_i32), ("diff", c_f64)]
 
 
 GLOBAL_FIELDS = ("t1_w", "t1_b", "t2_w", "t2_b", "mod_w", "mod_b", "txt_w", "txt_b",
@@ -72,6 +82,10 @@ _SIGS = {
     "dit_denoise_step": ([c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_f32, c_vp, c_vp], c_i32),
     "dit_denoise_step_cfg": ([c_vp, c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_f32, c_f32, c_vp,
                               c_vp], c_i32),
+    "dit_cache_begin": ([c_vp, ctypes.POINTER(dit_cache_params)], c_i32),
+    "dit_cache_state_get": ([c_vp, ctypes.POINTER(dit_cache_state)], c_i32),
+    "dit_denoise_step_cached": ([c_vp, c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_f32, c_f32, c_vp,
+                                 c_vp], c_i32),
     "dit_euler_step": ([c_vp, c_vp, c_i64, c_f32, c_f32, c_vp], c_i32),
     "dit_flow_sigmas": ([c_i32, c_f64, ctypes.POINTER(c_f64)], c_i32),
     "dit_attention": ([c_i32, c_i32, c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64,
@@ -125,15 +139,17 @@ def dit_status_string(status: int) -> str:
     return status_string(status)
 
 
-def make_config(cfg, guidance: bool = False, offload: bool = False) -> dit_config:
+def make_config(cfg, guidance: bool = False, offload: bool = False,
+                cache: bool = False) -> dit_config:
     """dit_config from any object with the workload attributes (hidden, heads,
     head_dim, mlp_hidden, num_blocks, in_channels, patch, latent, rope,
     ctx_len, text_dim, freq_dim, rope_theta, ln_eps, dtype); guidance sizes
     the workspace for guided steps; offload streams the block weights from
-    page-locked host memory."""
+    page-locked host memory; cache sizes the workspace for cached steps."""
     c = dit_config()
     c.guidance = 1 if guidance else 0
     c.offload = 1 if offload else 0
+    c.cache = 1 if cache else 0
     c.num_blocks, c.hidden, c.heads, c.head_dim = cfg.num_blocks, cfg.hidden, cfg.heads, cfg.head_dim
     c.mlp_hidden, c.freq_dim, c.in_channels = cfg.mlp_hidden, cfg.freq_dim, cfg.in_channels
     c.patch_f, c.patch_h, c.patch_w = cfg.patch
@@ -179,6 +195,34 @@ def dit_denoise_step_cfg(handle: int, X: int, ctx: int, ctx_neg: int, ctx_len: i
                          v_out: int | None = None, stream: int = 0) -> None:
     _check(lib().dit_denoise_step_cfg(handle, X, ctx, ctx_neg, ctx_len, t, sigma, sigma_next,
                                       guidance_scale, v_out, stream), "dit_denoise_step_cfg")
+
+
+def make_cache_params(fn: int = 2, bn: int = 1, warmup: int = 4, rdt: float = 0.4,
+                      max_consecutive: int = 4, taylorseer: bool = True,
+                      ts_order: int = 2) -> dit_cache_params:
+    """dit_cache_params; the defaults are the knob values of the pages'
+    Cache-DiT deployment."""
+    p = dit_cache_params()
+    p.fn, p.bn, p.warmup, p.rdt = fn, bn, warmup, rdt
+    p.max_consecutive, p.taylorseer, p.ts_order = max_consecutive, 1 if taylorseer else 0, ts_order
+    return p
+
+
+def dit_cache_begin(handle: int, params: dit_cache_params) -> None:
+    _check(lib().dit_cache_begin(handle, ctypes.byref(params)), "dit_cache_begin")
+
+
+def dit_cache_state_get(handle: int) -> dit_cache_state:
+    st = dit_cache_state()
+    _check(lib().dit_cache_state_get(handle, ctypes.byref(st)), "dit_cache_state_get")
+    return st
+
+
+def dit_denoise_step_cached(handle: int, X: int, ctx: int, ctx_neg: int | None, ctx_len: int,
+                            t: float, sigma: float, sigma_next: float, guidance_scale: float = 1.0,
+                            v_out: int | None = None, stream: int = 0) -> None:
+    _check(lib().dit_denoise_step_cached(handle, X, ctx, ctx_neg, ctx_len, t, sigma, sigma_next,
+                                         guidance_scale, v_out, stream), "dit_denoise_step_cached")
 
 
 def dit_euler_step(X: int, v: int, n: int, sigma: float, sigma_next: float, stream: int = 0) -> None:

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, "libdit.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "pointwise.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "pointwise.hip", "cache.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",

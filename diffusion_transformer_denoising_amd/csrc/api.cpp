@@ -41,6 +41,11 @@ struct Plan {
   // other block weights stream through two slots, field f of a slot at
   // slot[s] + wofs[f] (fields in dit_block_weights order; table unused)
   size_t tables, slot[2], wofs[15], wbytes[15];
+  // block caching across steps (float, NB S D elements each): h_0 and then
+  // h_fn of the current step, the probes of the current and the reference
+  // step (two buffers that swap roles), three Taylor factors of the middle
+  // residual, and the probe's per-workgroup partial sums (double)
+  size_t ch0, cprobe[2], ctf, cpart;
   size_t total;
 };
 
@@ -107,6 +112,15 @@ bool plan_layout(const dit_config &c, Plan &p) {
     p.slot[0] = take(sb);
     p.slot[1] = take(sb);
   }
+  p.ch0 = p.cprobe[0] = p.cprobe[1] = p.ctf = p.cpart = 0;
+  if (c.cache) {
+    const size_t n = f4 * NB * p.S * p.D;
+    p.ch0 = take(n);
+    p.cprobe[0] = take(n);
+    p.cprobe[1] = take(n);
+    p.ctf = take(3 * n);
+    p.cpart = take(2 * sizeof(double) * CACHE_PROBE_MAX_WG);
+  }
   p.total = off;
   return true;
 }
@@ -137,6 +151,7 @@ dit_status check_config(const dit_config *c) {
   if (S > (int64_t)1 << 30) return DIT_ERR_UNSUPPORTED;
   if (c->guidance != 0 && c->guidance != 1) return DIT_ERR_INVALID_ARG;
   if (c->offload != 0 && c->offload != 1) return DIT_ERR_INVALID_ARG;
+  if (c->cache != 0 && c->cache != 1) return DIT_ERR_INVALID_ARG;
   // guided steps stack two sequences; the transposed values are written in
   // runs of 8 rows, which must not straddle them
   if (c->guidance && S % 8) return DIT_ERR_UNSUPPORTED;
@@ -180,13 +195,13 @@ dit_status hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_
 enum ProfKind {
   PK_LN = 0, PK_GEMM_QKV, PK_ATTN_SELF, PK_GEMM_O, PK_GEMM_CQ, PK_GEMM_CKV,
   PK_ATTN_CROSS, PK_GEMM_CO, PK_GEMM_MLP1, PK_GEMM_MLP2, PK_TIME, PK_GEMM_TXT, PK_PATCHIFY,
-  PK_GEMM_PE, PK_GEMM_OUT, PK_EULER, PK_COUNT
+  PK_GEMM_PE, PK_GEMM_OUT, PK_EULER, PK_CACHE_PROBE, PK_CACHE_APPLY, PK_CACHE_UPDATE, PK_COUNT
 };
 const char *const kProfNames[PK_COUNT] = {
     "layernorm_modulate", "gemm_qkv_rope", "attention_self", "gemm_o", "gemm_cross_q",
     "gemm_cross_kv", "attention_cross", "gemm_cross_o", "gemm_mlp1_gelu", "gemm_mlp2",
     "time_embedding", "gemm_text_proj", "patchify", "gemm_patch_embed", "gemm_head",
-    "unpatchify_euler"};
+    "unpatchify_euler", "cache_probe", "cache_apply", "cache_update"};
 
 // Optional per-launch timing: a start and an end event recorded on the launch
 // stream around each kernel.  Events are created on demand and reused.
@@ -222,6 +237,14 @@ struct dit_model {
   // slot s filled, freed[s] the end of the last block that read it
   hipStream_t copy_stream = nullptr;
   hipEvent_t ready[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  // block caching: the knobs and decision state of the current run (valid
+  // while cache_ok), the probe buffer holding the reference, the sequence
+  // count of the run, and host room for the probe's partial sums
+  dit_cache_params cache_params{};
+  dit_cache_state cache_state{};
+  bool cache_ok = false;
+  int cache_ref = 0, cache_nb = 0;
+  std::vector<double> cache_part;
   template <typename U> U *buf(size_t off) const { return reinterpret_cast<U *>(ws + off); }
   ~dit_model() {
     for (int i = 0; i < 2; ++i) {
@@ -513,23 +536,25 @@ dit_status dit_block_forward(dit_model *m, int32_t block, float *x, const void *
 
 namespace {
 
-// One denoise step over nb sequences that share the latents X and the
-// timestep and differ in their context: ctx[n] for sequence n.  nb = 2 is the
-// guided step: sequence 0 takes the positive embeddings, 1 the negative ones,
-// and the Euler update uses v_neg + g (v_pos - v_neg).
-dit_status run_step(dit_model *m, float *X, const void *const *ctx, int nb, int ctx_len, float t,
-                    float sigma, float sigma_next, float g, float *v_out, hipStream_t s) {
+// The start of a denoise step over nb sequences that share the latents X and
+// the timestep and differ in their context ctx[n]: time path, context
+// projection (cproj[n] receives where sequence n's projected context sits),
+// patch embedding into every sequence's rows of x, and the cross K / V^T of
+// every block.  nb = 2 is the guided step: sequence 0 takes the positive
+// embeddings, 1 the negative ones.
+dit_status step_prologue(dit_model *m, float *X, const void *const *ctx, int nb, int ctx_len,
+                         float t, const void **cproj, hipStream_t s) {
   const dit_config &c = m->cfg;
   const Plan &p = m->plan;
-  const int S = (int)p.S, D = (int)p.D, P = (int)p.P, R = nb * S, B = c.num_blocks;
-  float *bmod = m->buf<float>(p.bmod), *hmod = m->buf<float>(p.hmod);
-  float *temb = m->buf<float>(p.temb), *x = m->buf<float>(p.x), *u = m->buf<float>(p.u);
-
-  dit_status st = run_time_path(m, t, bmod, hmod, temb, s);
+  const int S = (int)p.S, D = (int)p.D, P = (int)p.P, B = c.num_blocks;
+  float *x = m->buf<float>(p.x);
+  dit_status st = run_time_path(m, t, m->buf<float>(p.bmod), m->buf<float>(p.hmod),
+                                m->buf<float>(p.temb), s);
   if (st != DIT_OK) return st;
 
   // projected context n at c + n * L_max * D (or the caller's tokens)
-  const void *cproj[2] = {ctx[0], nb > 1 ? ctx[1] : nullptr};
+  cproj[0] = ctx[0];
+  cproj[1] = nb > 1 ? ctx[1] : nullptr;
   if (c.text_dim != c.hidden) {
     for (int n = 0; n < nb; ++n) {
       void *cn = m->buf<char>(p.c) + p.es * (size_t)n * c.ctx_len_max * D;
@@ -570,36 +595,59 @@ dit_status run_step(dit_model *m, float *X, const void *const *ctx, int nb, int 
     a.seg_gstride[1] = (int64_t)D * p.L_pad;
     DIT_RUN(m, PK_GEMM_CKV, s, launch_gemm(m->dt, EPI_SPLIT, a, s));
   }
-  if (!c.offload) {
-    for (int b = 0; b < B; ++b) {
-      st = run_block(m, m->blocks[b], b, x, cproj, ctx_len, bmod + (int64_t)b * 6 * D, s, true, nb);
+  return DIT_OK;
+}
+
+// Blocks [lo, hi) on the residual stream x of nb sequences.
+dit_status run_blocks(dit_model *m, int lo, int hi, const void *const *cproj, int ctx_len,
+                      hipStream_t s, int nb) {
+  const Plan &p = m->plan;
+  const int64_t D = p.D;
+  float *x = m->buf<float>(p.x);
+  const float *bmod = m->buf<float>(p.bmod);
+  dit_status st = DIT_OK;
+  if (!m->cfg.offload) {
+    for (int b = lo; b < hi; ++b) {
+      st = run_block(m, m->blocks[b], b, x, cproj, ctx_len, bmod + b * 6 * D, s, true, nb);
       if (st != DIT_OK) return st;
     }
-  } else {
-    // Layerwise offload: block b runs from slot b & 1 while block b + 1 is
-    // copied into the other; block b + 2's copy waits for block b's end.
-    // Both slots are free once the stream reaches this point.
-    hipStream_t cs = m->copy_stream;
-    for (int k = 0; k < 2; ++k) DIT_TRY(hipEventRecord(m->freed[k], s));
-    for (int b = 0; b < B && b < 2; ++b) {
-      DIT_TRY(hipStreamWaitEvent(cs, m->freed[b], 0));
-      DIT_TRY(copy_block(m, b, b, cs));
-      DIT_TRY(hipEventRecord(m->ready[b], cs));
-    }
-    for (int b = 0; b < B; ++b) {
-      const int sl = b & 1;
-      DIT_TRY(hipStreamWaitEvent(s, m->ready[sl], 0));
-      st = run_block(m, slot_weights(m, sl, b), b, x, cproj, ctx_len, bmod + (int64_t)b * 6 * D,
-                     s, false, nb);
-      if (st != DIT_OK) return st;
-      if (b + 2 < B) {
-        DIT_TRY(hipEventRecord(m->freed[sl], s));
-        DIT_TRY(hipStreamWaitEvent(cs, m->freed[sl], 0));
-        DIT_TRY(copy_block(m, b + 2, sl, cs));
-        DIT_TRY(hipEventRecord(m->ready[sl], cs));
-      }
+    return DIT_OK;
+  }
+  // Layerwise offload: block lo + i runs from slot i & 1 while the next block
+  // is copied into the other; the copy two blocks ahead waits for the end of
+  // the block that last read its slot.  Both slots are free once the stream
+  // reaches this point.
+  hipStream_t cs = m->copy_stream;
+  for (int k = 0; k < 2; ++k) DIT_TRY(hipEventRecord(m->freed[k], s));
+  for (int i = 0; i < 2 && lo + i < hi; ++i) {
+    DIT_TRY(hipStreamWaitEvent(cs, m->freed[i], 0));
+    DIT_TRY(copy_block(m, lo + i, i, cs));
+    DIT_TRY(hipEventRecord(m->ready[i], cs));
+  }
+  for (int b = lo; b < hi; ++b) {
+    const int sl = (b - lo) & 1;
+    DIT_TRY(hipStreamWaitEvent(s, m->ready[sl], 0));
+    st = run_block(m, slot_weights(m, sl, b), b, x, cproj, ctx_len, bmod + b * 6 * D, s, false,
+                   nb);
+    if (st != DIT_OK) return st;
+    if (b + 2 < hi) {
+      DIT_TRY(hipEventRecord(m->freed[sl], s));
+      DIT_TRY(hipStreamWaitEvent(cs, m->freed[sl], 0));
+      DIT_TRY(copy_block(m, b + 2, sl, cs));
+      DIT_TRY(hipEventRecord(m->ready[sl], cs));
     }
   }
+  return DIT_OK;
+}
+
+// The end of a step: final layer on every sequence, then the Euler update with
+// the velocity of sequence 0 or, for nb = 2, v_neg + g (v_pos - v_neg).
+dit_status step_epilogue(dit_model *m, float *X, int nb, float sigma, float sigma_next, float g,
+                         float *v_out, hipStream_t s) {
+  const dit_config &c = m->cfg;
+  const Plan &p = m->plan;
+  const int S = (int)p.S, D = (int)p.D, P = (int)p.P, R = nb * S;
+  float *hmod = m->buf<float>(p.hmod), *x = m->buf<float>(p.x), *u = m->buf<float>(p.u);
   DIT_RUN(m, PK_LN, s, launch_ln_modulate(m->dt, x, R, D, c.ln_eps, hmod, hmod + D, m->buf<void>(p.y), s));
   {
     GemmArgs a = gemm(m->buf<void>(p.y), D, m->g.out_w, D, R, P, D, m->g.out_b);
@@ -610,6 +658,93 @@ dit_status run_step(dit_model *m, float *X, const void *const *ctx, int nb, int 
   DIT_RUN(m, PK_EULER, s, launch_unpatchify_euler(u, nb > 1 ? u + (size_t)S * P : nullptr, g, X, v_out,
                                   sigma_next - sigma, c.in_channels, c.lat_f, c.lat_h, c.lat_w,
                                   c.patch_f, c.patch_h, c.patch_w, s));
+  return DIT_OK;
+}
+
+dit_status run_step(dit_model *m, float *X, const void *const *ctx, int nb, int ctx_len, float t,
+                    float sigma, float sigma_next, float g, float *v_out, hipStream_t s) {
+  const void *cproj[2];
+  dit_status st = step_prologue(m, X, ctx, nb, ctx_len, t, cproj, s);
+  if (st == DIT_OK) st = run_blocks(m, 0, m->cfg.num_blocks, cproj, ctx_len, s, nb);
+  if (st == DIT_OK) st = step_epilogue(m, X, nb, sigma, sigma_next, g, v_out, s);
+  return st;
+}
+
+// A step with block caching (the rules are stated with dit_cache_params).
+// The first fn blocks run, then the probe kernel writes P = h_fn - h_0 and,
+// when the step may reuse the cache, the partial sums of its difference to
+// the reference probe, which the host reads back to decide.  A cached step
+// adds the Taylor stand-in for the middle residual; a full step runs the
+// middle blocks and refreshes the factors, and its probe becomes the
+// reference.  The last bn blocks and the final layer always run.
+dit_status run_step_cached(dit_model *m, float *X, const void *const *ctx, int nb, int ctx_len,
+                           float t, float sigma, float sigma_next, float g, float *v_out,
+                           hipStream_t s) {
+  const Plan &p = m->plan;
+  const dit_cache_params &cp = m->cache_params;
+  dit_cache_state &cs = m->cache_state;
+  const int B = m->cfg.num_blocks;
+  const int64_t n = (int64_t)nb * p.S * p.D;
+  float *x = m->buf<float>(p.x), *h0 = m->buf<float>(p.ch0), *tf = m->buf<float>(p.ctf);
+  float *probe_ref = m->buf<float>(p.cprobe[m->cache_ref]);
+  float *probe_cur = m->buf<float>(p.cprobe[1 - m->cache_ref]);
+  double *part = m->buf<double>(p.cpart);
+  m->cache_ok = false;  // until the step has been enqueued whole
+
+  const void *cproj[2];
+  dit_status st = step_prologue(m, X, ctx, nb, ctx_len, t, cproj, s);
+  if (st != DIT_OK) return st;
+  DIT_TRY(hipMemcpyAsync(h0, x, sizeof(float) * n, hipMemcpyDeviceToDevice, s));
+  st = run_blocks(m, 0, cp.fn, cproj, ctx_len, s, nb);
+  if (st != DIT_OK) return st;
+  const bool eligible = cs.step >= cp.warmup && cs.factors >= 1 &&
+                        cs.consecutive < cp.max_consecutive;
+  DIT_RUN(m, PK_CACHE_PROBE, s,
+          launch_cache_probe(x, h0, probe_cur, eligible ? probe_ref : nullptr, n, part, s));
+  bool hit = false;
+  double diff = -1.0;
+  if (eligible) {
+    const int G = cache_probe_groups(n);
+    m->cache_part.resize(2 * (size_t)G);
+    DIT_TRY(hipMemcpyAsync(m->cache_part.data(), part, 2 * sizeof(double) * G,
+                           hipMemcpyDeviceToHost, s));
+    DIT_TRY(hipStreamSynchronize(s));
+    double num = 0.0, den = 0.0;
+    for (int w = 0; w < G; ++w) {
+      num += m->cache_part[2 * w];
+      den += m->cache_part[2 * w + 1];
+    }
+    diff = den > 0.0 ? num / den : (num == 0.0 ? 0.0 : HUGE_VAL);
+    hit = diff < (double)cp.rdt;
+  }
+  const int k = cs.step - cs.last_full;  // steps since the last full one
+  const int order = cp.taylorseer ? cp.ts_order : 0;
+  const int nnew = cs.factors + 1 < order + 1 ? cs.factors + 1 : order + 1;
+  if (hit) {
+    DIT_RUN(m, PK_CACHE_APPLY, s,
+            launch_cache_apply(x, tf, n, cs.factors, (float)k, 0.5f * (float)k * (float)k, s));
+  } else {
+    st = run_blocks(m, cp.fn, B - cp.bn, cproj, ctx_len, s, nb);
+    if (st != DIT_OK) return st;
+    DIT_RUN(m, PK_CACHE_UPDATE, s, launch_cache_update(x, h0, tf, n, nnew, (float)k, s));
+  }
+  st = run_blocks(m, B - cp.bn, B, cproj, ctx_len, s, nb);
+  if (st == DIT_OK) st = step_epilogue(m, X, nb, sigma, sigma_next, g, v_out, s);
+  if (st != DIT_OK) return st;
+
+  if (hit) {
+    cs.consecutive += 1;
+    cs.cached_total += 1;
+  } else {
+    cs.consecutive = 0;
+    cs.last_full = cs.step;
+    cs.factors = nnew;
+    m->cache_ref = 1 - m->cache_ref;  // this step's probe is the new reference
+  }
+  cs.hit = hit ? 1 : 0;
+  cs.diff = diff;
+  cs.step += 1;
+  m->cache_ok = true;
   return DIT_OK;
 }
 
@@ -648,6 +783,49 @@ dit_status dit_denoise_step_cfg(dit_model *m, float *X, const void *ctx, const v
   const void *ctxs[2] = {ctx, ctx_neg};
   return run_step(m, X, ctxs, 2, ctx_len, t, sigma, sigma_next, guidance_scale, v_out,
                   static_cast<hipStream_t>(stream));
+}
+
+dit_status dit_cache_begin(dit_model *m, const dit_cache_params *cp) {
+  if (!m || !cp) return DIT_ERR_INVALID_ARG;
+  if (!m->cfg.cache) return DIT_ERR_WORKSPACE;
+  if (cp->warmup < 0 || cp->max_consecutive < 0 || !(cp->rdt >= 0.0f) ||
+      (cp->taylorseer != 0 && cp->taylorseer != 1) || cp->ts_order < 0)
+    return DIT_ERR_INVALID_ARG;
+  if (cp->fn < 1 || cp->bn < 0 || (int64_t)cp->fn + cp->bn > m->cfg.num_blocks) return DIT_ERR_SHAPE;
+  if (cp->taylorseer && cp->ts_order > 2) return DIT_ERR_UNSUPPORTED;
+  m->cache_params = *cp;
+  m->cache_state = dit_cache_state{};
+  m->cache_state.last_full = -1;
+  m->cache_state.diff = -1.0;
+  m->cache_ref = 0;
+  m->cache_nb = 0;
+  m->cache_ok = true;
+  return DIT_OK;
+}
+
+dit_status dit_cache_state_get(const dit_model *m, dit_cache_state *out) {
+  if (!m || !out) return DIT_ERR_INVALID_ARG;
+  if (!m->cfg.cache) return DIT_ERR_WORKSPACE;
+  *out = m->cache_state;
+  return DIT_OK;
+}
+
+dit_status dit_denoise_step_cached(dit_model *m, float *X, const void *ctx, const void *ctx_neg,
+                                   int32_t ctx_len, float t, float sigma, float sigma_next,
+                                   float guidance_scale, float *v_out, void *stream) {
+  dit_status st = check_step(m, X, ctx_len, t, sigma, sigma_next, v_out);
+  if (st != DIT_OK) return st;
+  if (!ok_ptr(ctx) || (ctx_neg && !aligned16(ctx_neg)) || !std::isfinite(guidance_scale))
+    return DIT_ERR_INVALID_ARG;
+  if (!m->cfg.cache || (ctx_neg && !m->cfg.guidance)) return DIT_ERR_WORKSPACE;
+  if (!m->cache_ok) return DIT_ERR_INVALID_ARG;  // no run begun, or the last step failed
+  const int nb = ctx_neg ? 2 : 1;
+  // the cached residuals are per sequence: one run keeps one sequence count
+  if (m->cache_nb != 0 && m->cache_nb != nb) return DIT_ERR_SHAPE;
+  m->cache_nb = nb;
+  const void *ctxs[2] = {ctx, ctx_neg};
+  return run_step_cached(m, X, ctxs, nb, ctx_len, t, sigma, sigma_next, guidance_scale, v_out,
+                         static_cast<hipStream_t>(stream));
 }
 
 dit_status dit_euler_step(float *X, const float *v, int64_t n, float sigma, float sigma_next,

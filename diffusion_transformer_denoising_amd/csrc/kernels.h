@@ -111,4 +111,20 @@ hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, f
                        int N, int K, bool silu_in, const void *const *fan, int nfan, float *fan_out,
                        hipStream_t s);
 
+// Block caching across steps (float [n] buffers, n a multiple of 4).
+// Probe: probe = x - h0, then h0 = x; with ref (nullable) workgroup w writes
+// sum |probe - ref| and sum |ref| to partials[2w], partials[2w + 1], over
+// cache_probe_groups(n) <= CACHE_PROBE_MAX_WG workgroups.
+constexpr int CACHE_PROBE_MAX_WG = 2048;
+int cache_probe_groups(int64_t n);
+hipError_t launch_cache_probe(const float *x, float *h0, float *probe, const float *ref, int64_t n,
+                              double *partials, hipStream_t s);
+// x += T_0 + c1 T_1 + c2 T_2 over the first nf (1..3) factors, factor q at tf + q n.
+hipError_t launch_cache_apply(float *x, const float *tf, int64_t n, int nf, float c1, float c2,
+                              hipStream_t s);
+// After a full step: T_0 = x - hf and T_q = (new T_{q-1} - old T_{q-1}) / gap for
+// q < nnew (1..3), in place.
+hipError_t launch_cache_update(const float *x, const float *hf, float *tf, int64_t n, int nnew,
+                               float gap, hipStream_t s);
+
 }  // namespace dit

@@ -66,10 +66,11 @@ def gemm(dtype: str, epilogue: int, A, W, bias, out, gate=None, tile: int = 0, s
 
 class DeviceDiT:
     def __init__(self, cfg, params: dict, device: str = "cuda", stream: int | None = None,
-                 guidance: bool = False, offload: bool = False, pack_offload: bool = True):
+                 guidance: bool = False, offload: bool = False, pack_offload: bool = True,
+                 cache: bool = False):
         self.cfg = cfg
         self.device = torch.device(device)
-        self.c = B.make_config(cfg, guidance, offload)
+        self.c = B.make_config(cfg, guidance, offload, cache)
         g = params["global"]
         self._keep = []
 
@@ -167,6 +168,34 @@ class DeviceDiT:
                                ctx.shape[0], t, sigma, sigma_next, guidance_scale,
                                v_out.data_ptr() if v_out is not None else None,
                                self._stream(stream))
+
+    def cache_begin(self, **knobs):
+        """Start a cached sampling run (model built with cache=True); knobs as
+        binding.make_cache_params."""
+        B.dit_cache_begin(self.handle, B.make_cache_params(**knobs))
+
+    def cache_state(self) -> dict:
+        st = B.dit_cache_state_get(self.handle)
+        return {n: getattr(st, n) for n, _ in B.dit_cache_state._fields_}
+
+    def denoise_step_cached(self, X: torch.Tensor, ctx: torch.Tensor, t: float, sigma: float,
+                            sigma_next: float, ctx_neg: torch.Tensor | None = None,
+                            guidance_scale: float = 1.0, v_out: torch.Tensor | None = None,
+                            stream=None):
+        """One step of the cached run (guided when ctx_neg is given)."""
+        self._check(X, torch.float32)
+        self._check(ctx, torch_dtype(self.cfg))
+        if ctx_neg is not None:
+            self._check(ctx_neg, torch_dtype(self.cfg))
+            if ctx_neg.shape != ctx.shape:
+                raise ValueError("positive and negative contexts must have the same shape")
+        if v_out is not None:
+            self._check(v_out, torch.float32)
+        B.dit_denoise_step_cached(self.handle, X.data_ptr(), ctx.data_ptr(),
+                                  ctx_neg.data_ptr() if ctx_neg is not None else None,
+                                  ctx.shape[0], t, sigma, sigma_next, guidance_scale,
+                                  v_out.data_ptr() if v_out is not None else None,
+                                  self._stream(stream))
 
     def block_forward(self, block: int, x: torch.Tensor, ctx: torch.Tensor, mod: torch.Tensor,
                       stream=None):

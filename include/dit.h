@@ -100,6 +100,8 @@ typedef struct {
                            the previous one, are moved in a single transfer;
                            any other placement is valid but copied field by
                            field.  0: all weights resident on the device    */
+  int32_t cache;        /* 1: size the workspace for cached steps
+                           (dit_denoise_step_cached); 0: none               */
 } dit_config;
 
 /* Model-wide parameters (device pointers, element type T).  Shapes:
@@ -196,6 +198,71 @@ dit_status dit_denoise_step(dit_model *model, float *X, const void *ctx, int32_t
 dit_status dit_denoise_step_cfg(dit_model *model, float *X, const void *ctx, const void *ctx_neg,
                                 int32_t ctx_len, float t, float sigma, float sigma_next,
                                 float guidance_scale, float *v_out, void *stream);
+
+/* Block caching across the steps of one sampling run (page "Disaggregated
+ * Diffusion Pipeline", section "GLM-Image distributed mode": the denoisers
+ * run with Cache-DiT and the knobs FN, BN, WARMUP, RDT, MC, TAYLORSEER and
+ * TS_ORDER, values 2, 1, 4, 0.4, 4, true, 2; the page names the knobs only,
+ * and the rules below are the reading of those names).
+ *
+ * Every step runs the first `fn` blocks.  Their residual P = h_fn - h_0 (the
+ * stream after them minus the embedded tokens) is compared with P_ref, the
+ * same residual on the last step that ran every block: d = sum|P - P_ref| /
+ * sum|P_ref|.  A step reuses the cache when (a) it is not one of the first
+ * `warmup` steps, (b) an earlier step ran every block, (c) fewer than
+ * `max_consecutive` steps in a row have reused it, and (d) d < rdt.  It then
+ * skips the middle blocks [fn, num_blocks - bn) and adds a stand-in for their
+ * residual M = h_{num_blocks-bn} - h_fn instead: with TaylorSeer, sum_q T_q
+ * k^q / q! over the factors in hand (k = steps since the last full step),
+ * where after each full step T_0 = M and T_q = (T_{q-1} - previous
+ * T_{q-1}) / (steps between the two full steps), q <= ts_order; without
+ * TaylorSeer, the last M.  The last `bn` blocks always run.  Guided steps make
+ * one decision for both sequences (d sums over both) and keep one residual
+ * cache per sequence. */
+typedef struct {
+  int32_t fn;              /* first blocks run on every step, >= 1        */
+  int32_t bn;              /* last blocks run on every step, >= 0;
+                              fn + bn <= num_blocks                        */
+  int32_t warmup;          /* steps that always run every block, >= 0     */
+  float rdt;               /* threshold on d, >= 0 (+inf allowed)          */
+  int32_t max_consecutive; /* cached steps in a row at most, >= 0         */
+  int32_t taylorseer;      /* 1: Taylor extrapolation of the residual      */
+  int32_t ts_order;        /* 0 .. 2                                       */
+} dit_cache_params;
+
+/* The decision state after the last cached-path step. */
+typedef struct {
+  int32_t step;            /* steps taken since dit_cache_begin            */
+  int32_t consecutive;     /* cached steps since the last full one         */
+  int32_t last_full;       /* index of the last full step, -1 before any   */
+  int32_t factors;         /* Taylor factors in hand (0: nothing cached)   */
+  int32_t hit;             /* last step: 1 reused the cache, 0 ran it all  */
+  int32_t cached_total;    /* steps that reused the cache                  */
+  double diff;             /* last step's d; -1 when the step could not
+                              reuse the cache and d was not measured       */
+} dit_cache_state;
+
+/* Start a sampling run: validate and keep the knobs, clear the state (host
+ * call, no device work).  Needs a handle created with cache = 1 (else
+ * DIT_ERR_WORKSPACE); invalid knobs give DIT_ERR_INVALID_ARG, fn + bn >
+ * num_blocks DIT_ERR_SHAPE, ts_order > 2 DIT_ERR_UNSUPPORTED. */
+dit_status dit_cache_begin(dit_model *model, const dit_cache_params *params);
+
+/* Copy the decision state to *state (host call). */
+dit_status dit_cache_state_get(const dit_model *model, dit_cache_state *state);
+
+/* One step of the run begun by dit_cache_begin: dit_denoise_step (ctx_neg
+ * NULL) or dit_denoise_step_cfg (ctx_neg given; the handle also needs
+ * guidance = 1) with the block cache above.  Arguments as there.  When the
+ * step could reuse the cache it waits once for `stream` to reach the probe
+ * and reads 2 doubles per probe workgroup back to the host to decide; other
+ * steps do not synchronise.  The cached residuals live in their own part of
+ * the workspace, which other calls on the handle leave alone.  On an error
+ * the run must be begun again. */
+dit_status dit_denoise_step_cached(dit_model *model, float *X, const void *ctx,
+                                   const void *ctx_neg, int32_t ctx_len, float t, float sigma,
+                                   float sigma_next, float guidance_scale, float *v_out,
+                                   void *stream);
 
 /* Flow Euler update X[i] += (sigma_next - sigma) * v[i] for i < n on device
  * float arrays (layout-agnostic).  n == 0 is a no-op. */

@@ -160,3 +160,28 @@ def test_offload_workspace_and_validation():
     with pytest.raises(B.DitError) as e:
         B.dit_workspace_size(c)
     assert e.value.status == B.DIT_ERR_INVALID_ARG
+
+
+def test_cache_workspace_and_validation():
+    # Cached steps keep h_0 / h_fn, two probes and three Taylor factors (float,
+    # one row per token of every sequence) plus the probe's partial sums.
+    for cfg in CONFIGS.values():
+        for guided in (False, True):
+            if guided and cfg.tokens % 8:
+                continue
+            nb = 2 if guided else 1
+            base = B.dit_workspace_size(B.make_config(cfg, guidance=guided))
+            cached = B.dit_workspace_size(B.make_config(cfg, guidance=guided, cache=True))
+            need = 6 * 4 * nb * cfg.tokens * cfg.hidden + 2 * 8 * 2048
+            assert need <= cached - base <= need + 6 * 256
+    c = B.make_config(CONFIGS["image_s_bf16"], cache=True)
+    c.cache = 2
+    with pytest.raises(B.DitError) as e:
+        B.dit_workspace_size(c)
+    assert e.value.status == B.DIT_ERR_INVALID_ARG
+    L = B.lib()
+    p = B.make_cache_params()
+    assert L.dit_cache_begin(None, ctypes.byref(p)) == B.DIT_ERR_INVALID_ARG
+    assert L.dit_cache_state_get(None, None) == B.DIT_ERR_INVALID_ARG
+    assert L.dit_denoise_step_cached(None, 4096, 4096, None, 1, 1.0, 1.0, 0.0, 1.0, None,
+                                     None) == B.DIT_ERR_INVALID_ARG
