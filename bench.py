@@ -65,11 +65,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kind_work(cfg, nb: int = 1) -> dict:
+def kind_work(cfg, nb: int = 1, offload: bool = False) -> dict:
     """Algorithmic work per launch of each kernel kind: ("flop", n) for matrix-core
     kernels, ("byte", n) for bandwidth-bound ones (minimum HBM traffic).  nb = 2
     is the guided step: the block kernels and the head process two stacked
-    sequences per launch, the context kernels run once per context."""
+    sequences per launch, the context kernels run once per context.  With
+    offload each block projects its own cross K / V."""
     S, D, F, L, P = cfg.tokens, cfg.hidden, cfg.mlp_hidden, cfg.ctx_len, cfg.patch_dim
     R = nb * S
     es = 2 if cfg.dtype == "bf16" else 4
@@ -79,7 +80,7 @@ def kind_work(cfg, nb: int = 1) -> dict:
         "gemm_o": ("flop", 2 * R * D * D),
         "gemm_cross_q": ("flop", 2 * R * D * D),
         # one grouped launch per context computes every block's cross K / V^T
-        "gemm_cross_kv": ("flop", cfg.num_blocks * 2 * L * D * 2 * D),
+        "gemm_cross_kv": ("flop", (1 if offload else cfg.num_blocks) * 2 * L * D * 2 * D),
         "gemm_cross_o": ("flop", 2 * R * D * D),
         "gemm_mlp1_gelu": ("flop", 2 * R * D * F),
         "gemm_mlp2": ("flop", 2 * R * F * D),
@@ -95,6 +96,13 @@ def kind_work(cfg, nb: int = 1) -> dict:
         "unpatchify_euler": ("byte", n_lat * 4 * (nb + 2)),
         # three GEMV launches per step; the per-launch figure is their mean
         "time_embedding": ("byte", es * (cfg.freq_dim * D + D * D + 6 * D * D) // 3),
+        # block caching, float buffers of R * D elements: the probe reads x, h_0
+        # and the reference and writes the probe and h_fn; with three Taylor
+        # factors in hand the stand-in reads x and the factors and writes x, and
+        # the update reads x, h_fn and the factors and writes the factors
+        "cache_probe": ("byte", 20 * R * D),
+        "cache_apply": ("byte", 20 * R * D),
+        "cache_update": ("byte", 32 * R * D),
     }
 
 
@@ -247,7 +255,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     B.dit_profile_enable(m.handle, False)
     prof = B.profile_summary(m.handle)
-    work = kind_work(cfg, nb)
+    work = kind_work(cfg, nb, args.offload)
     kernels = {}
     for name, (n, tms) in sorted(prof.items(), key=lambda kv: -kv[1][1]):
         unit, amount = work.get(name, ("flop", 0))
