@@ -7,8 +7,9 @@
 // to separate buffers (transposed for the attention values, rotated by RoPE
 // for q and k).
 //
-// A 256-thread workgroup (4 waves as 2 x 2) owns a BM x BN output tile; each
-// wave owns (BM/2) x (BN/2) as 32x32 MFMA tiles.  Two main loops:
+// A workgroup owns a BM x BN output tile, split over its waves as 32x32 MFMA
+// tiles: 8 waves as 2 x 4 (each 128 x 64; two waves per SIMD) for the default
+// 256x256 tile, 4 waves as 2 x 2 for the others.  Two main loops:
 //   gemm_kernel (256x256 bf16, 64x64 fp32): 128-byte K slices staged through
 //     registers into double-buffered, row-padded LDS; the instruction order
 //     of a K step is pinned (sched_group_barrier) so fragment reads, staging
