@@ -351,7 +351,7 @@ __device__ __forceinline__ void att_exp_half(const f32x16 &x, bf16x8 &lo, bf16x8
   }
 }
 
-template <int HD, int NW>
+template <int HD, int NW, int KS = 1>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kernel(AttnArgs p) {
   att_select_batch(p, 2);
   typedef bf16x8 F;
@@ -360,11 +360,16 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
   constexpr int KBYTES = ATT_BK * KROWB;   // K tile
   constexpr int VBYTES = HD * ATT_BK * 2;  // V^T tile (rows of 128 bytes)
   constexpr int KPIECES = KBYTES / 16, VPIECES = VBYTES / 16;
-  constexpr int KINSTR = KPIECES / (64 * NW), VINSTR = VPIECES / (64 * NW);
-  static_assert(KINSTR >= 1 && VINSTR >= 1 && KPIECES % (64 * NW) == 0, "tile split");
+  // KS key ranges: the workgroup's waves form KS groups of NWG; the waves of
+  // a group cover NWG different 32-query blocks over one key range with their
+  // own K/V ring, and wave w of every group holds the same queries, so the
+  // groups' partial results are merged through LDS at the end.
+  static_assert(KS == 1 || KS == 2, "key split");
+  constexpr int NWG = NW / KS;
+  constexpr int KINSTR = KPIECES / (64 * NWG), VINSTR = VPIECES / (64 * NWG);
+  static_assert(KINSTR >= 1 && VINSTR >= 1 && KPIECES % (64 * NWG) == 0, "tile split");
   constexpr int QCH = HD / 16;
   constexpr int DT = HD / 32;
-  constexpr int NT = 64 * NW;
   constexpr int NQK = 2 * QCH;             // S MFMAs per tile
   constexpr int NPV = 4 * DT;              // P.V MFMAs per tile
   // vector instructions per MFMA slot: phase A has 32 (16 exp, 8 pack, 8 dot),
@@ -372,14 +377,17 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
   constexpr int VA = (32 + NQK - 1) / NQK, VB = (64 + NPV - 1) / NPV;
   constexpr float PSUM_MAX = 65536.0f;
 
-  // [K stage 0][K stage 1][V^T stage 0][V^T stage 1]
-  __shared__ __attribute__((aligned(1024))) char lds[2 * KBYTES + 2 * VBYTES];
+  // per key range: [K stage 0][K stage 1][V^T stage 0][V^T stage 1]
+  constexpr int RING = 2 * KBYTES + 2 * VBYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[KS * RING];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave / NWG, wig = wave % NWG;  // key range, wave within it
+  const int rbase = grp * RING;                  // LDS ring of this key range
   const int half = lane >> 5, l32 = lane & 31;
   const int head = blockIdx.y;
-  const int q0 = blockIdx.x * (32 * NW) + wave * 32;
+  const int q0 = blockIdx.x * (32 * NWG) + wig * 32;
   const int sq = p.sq, sk = p.sk;
   const bf16 *Q = static_cast<const bf16 *>(p.q) + head * HD;
 
@@ -388,11 +396,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
       att_rsrc(p.vt, (uint32_t)((int64_t)p.heads * HD * p.ldv * 2));
 
   // Per-lane global byte offsets of the pieces this lane moves (tile 0);
-  // piece P = (instr * NW + wave) * 64 + lane lands at LDS byte 16 P.
+  // piece P = (instr * NWG + wig) * 64 + lane lands at byte 16 P of the ring.
   uint32_t koff[KINSTR], voff[VINSTR];
 #pragma unroll
   for (int j = 0; j < KINSTR; ++j) {
-    const int P = (j * NW + wave) * 64 + lane;
+    const int P = (j * NWG + wig) * 64 + lane;
     const int row = P / KCHUNK, phys = P % KCHUNK;
     const int logical = phys ^ att_kswz<HD>(row);
     const int key = (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
@@ -400,23 +408,32 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
   }
 #pragma unroll
   for (int j = 0; j < VINSTR; ++j) {
-    const int P = (j * NW + wave) * 64 + lane;
+    const int P = (j * NWG + wig) * 64 + lane;
     const int row = P / 8, phys = P % 8;
     const int logical = phys ^ ((row >> 1) & 7);
     voff[j] = (uint32_t)((((int64_t)head * HD + row) * p.ldv + logical * 8) * 2);
   }
   const uint32_t kstep = (uint32_t)(ATT_BK * p.ldk * 2);
+  // key tiles of this range: n_tiles of them from global tile t_base; with
+  // two ranges every range gets the same count (barriers stay matched), the
+  // second one ending in a partial or an empty tile (all keys masked)
+  const int n_all = (sk + ATT_BK - 1) / ATT_BK;
+  const int n_tiles = KS == 1 ? n_all : (n_all + 1) / 2;
+  const int t_base = grp * n_tiles;
+  const bool ragged = (int64_t)(t_base + n_tiles) * ATT_BK > sk;
+  const bool ragged_wg = KS == 1 ? ragged : (int64_t)2 * n_tiles * ATT_BK > sk;  // the last range's
   auto issue_k = [&](int it, int slot) {
-    char *b = lds + slot * KBYTES;
+    char *b = lds + rbase + slot * KBYTES;
 #pragma unroll
     for (int j = 0; j < KINSTR; ++j)
-      lds_load16(krs, b + (j * NW + wave) * 1024, koff[j] + (uint32_t)it * kstep);
+      lds_load16(krs, b + (j * NWG + wig) * 1024, koff[j] + (uint32_t)(t_base + it) * kstep);
   };
   auto issue_v = [&](int it, int slot) {
-    char *b = lds + 2 * KBYTES + slot * VBYTES;
+    char *b = lds + rbase + 2 * KBYTES + slot * VBYTES;
 #pragma unroll
     for (int j = 0; j < VINSTR; ++j)
-      lds_load16(vrs, b + (j * NW + wave) * 1024, voff[j] + (uint32_t)it * (ATT_BK * 2));
+      lds_load16(vrs, b + (j * NWG + wig) * 1024,
+                 voff[j] + (uint32_t)(t_base + it) * (ATT_BK * 2));
   };
 
   // Q fragments stay in registers for the whole key loop.
@@ -440,9 +457,10 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
   {
     const int kswz = att_kswz<HD>(l32), vswz = (l32 >> 1) & 7;
 #pragma unroll
-    for (int ch = 0; ch < QCH; ++ch) kaddr[ch] = l32 * KROWB + (((ch * 2 + half) ^ kswz) * 16);
+    for (int ch = 0; ch < QCH; ++ch) kaddr[ch] = rbase + l32 * KROWB + (((ch * 2 + half) ^ kswz) * 16);
 #pragma unroll
-    for (int ch = 0; ch < 4; ++ch) vaddr[ch] = 2 * KBYTES + l32 * 128 + (((ch * 2 + half) ^ vswz) * 16);
+    for (int ch = 0; ch < 4; ++ch)
+      vaddr[ch] = rbase + 2 * KBYTES + l32 * 128 + (((ch * 2 + half) ^ vswz) * 16);
   }
 
   f32x16 o[DT];
@@ -452,9 +470,6 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
     for (int e = 0; e < 16; ++e) o[t][e] = 0.0f;
   const float c = p.scale_log2;
   float m_run, l_run = 0.0f;
-
-  const int n_tiles = (sk + ATT_BK - 1) / ATT_BK;
-  const bool ragged = (sk % ATT_BK) != 0;
 
   // S^T of the tile in K stage `slot` into s (raw scores)
   auto qk = [&](f32x16 (&s)[2], int slot) {
@@ -519,15 +534,19 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
     if (i + 2 < n_tiles) issue_k(i + 2, par);
     if (i + 1 < n_tiles) issue_v(i + 1, par ^ 1);
     if constexpr (!has_next) {
-      if (ragged) {
-        // clear V^T entries of keys past the end (inside the caller's rows)
-        bf16 *vt = reinterpret_cast<bf16 *>(lds + 2 * KBYTES + par * VBYTES);
-        const int valid = sk - i * ATT_BK;
-        for (int x = tid; x < HD * ATT_BK; x += NT) {
-          const int row = x / ATT_BK, key = x % ATT_BK;
-          if (key >= valid) {
-            const int phys = (key >> 3) ^ ((row >> 1) & 7);
-            vt[row * ATT_BK + phys * 8 + (key & 7)] = (bf16)0.0f;
+      // every wave of the workgroup takes this barrier when the last range
+      // ends short, so the counts match across ranges
+      if (ragged_wg) {
+        if (ragged) {
+          // clear V^T entries of keys past the end (inside the caller's rows)
+          bf16 *vt = reinterpret_cast<bf16 *>(lds + rbase + 2 * KBYTES + par * VBYTES);
+          const int valid = sk - (t_base + i) * ATT_BK;
+          for (int x = wig * 64 + lane; x < HD * ATT_BK; x += NWG * 64) {
+            const int row = x / ATT_BK, key = x % ATT_BK;
+            if (key >= valid) {
+              const int phys = (key >> 3) ^ ((row >> 1) & 7);
+              vt[row * ATT_BK + phys * 8 + (key & 7)] = (bf16)0.0f;
+            }
           }
         }
         __syncthreads();
@@ -561,7 +580,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) xn[mt][e] = fmaf(xn[mt][e], c, nm);
-      if constexpr (mask_next) mask(xn, (i + 1) * ATT_BK);
+      if constexpr (mask_next) mask(xn, (t_base + i + 1) * ATT_BK);
       ln = 0.0f;
       att_exp_half(xn[0], pn[0], pn[1], ln);
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
@@ -587,7 +606,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   qk(xa, 0);
-  if (n_tiles == 1 && ragged) mask(xa, 0);
+  if (n_tiles == 1 && ragged) mask(xa, t_base * ATT_BK);
   {
     float mx = xa[0][0];
 #pragma unroll
@@ -628,6 +647,32 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
   }
   step(std::false_type{}, std::false_type{}, xa, pa, la, xb, pb, lb, i, i & 1);
 
+  if constexpr (KS == 2) {
+    // merge the second key range into the first: with m the larger running
+    // max, O = O_0 2^(m_0 - m) + O_1 2^(m_1 - m) and the same for the sums
+    // (every range holds at least one key, so both maxima are finite)
+    float *mrg = reinterpret_cast<float *>(lds) + wig * (DT * 16 + 2) * 64;
+    __syncthreads();  // both rings are free
+    if (grp == 1) {
+      mrg[lane] = m_run;
+      mrg[64 + lane] = l_run;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mrg[(2 + t * 16 + e) * 64 + lane] = o[t][e];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = mrg[lane], l1 = mrg[64 + lane];
+    const float mn = fmaxf(m_run, m1);
+    const float a0 = fast_exp2(m_run - mn), a1 = fast_exp2(m1 - mn);
+    l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[t][e] = o[t][e] * a0 + mrg[(2 + t * 16 + e) * 64 + lane] * a1;
+  }
+
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = 1.0f / l_tot;
   const int qi = q0 + l32;
@@ -661,6 +706,17 @@ static hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
   const int64_t problems = (int64_t)a.heads * (a.batch > 1 ? a.batch : 1);
   while (nw > 1 && (int64_t)((a.sq + 32 * nw - 1) / (32 * nw)) * problems < 128) nw >>= 1;
   dim3 grid((a.sq + 32 * nw - 1) / (32 * nw), a.heads, a.batch > 1 ? a.batch : 1);
+  // Small grids (at most two waves per workgroup): split the keys in two
+  // ranges, each covered by its own set of waves for the same queries, so the
+  // workgroup runs twice the waves and every SIMD of its CU has work.  Needs
+  // at least two key tiles.
+  if (nw <= 2 && a.sk > ATT_BK) {
+    if (nw == 2)
+      attention_bf16_kernel<HD, 4, 2><<<grid, 256, 0, s>>>(a);
+    else
+      attention_bf16_kernel<HD, 2, 2><<<grid, 128, 0, s>>>(a);
+    return hipGetLastError();
+  }
   if constexpr (MAXNW == 8) {
     if (nw == 8) {
       attention_bf16_kernel<HD, 8><<<grid, 512, 0, s>>>(a);
