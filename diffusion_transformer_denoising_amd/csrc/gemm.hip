@@ -670,7 +670,14 @@ hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s,
       case 1: return launch_t<bf16, 256, 256>(epi, a, s);
       case 4: return launch_t<bf16, 256, 256, 4, 8>(epi, a, s);
       case 2: return launch_dl<128, 128, 4>(epi, a, s);
-      default: return launch_dl<64, 64, 5>(epi, a, s);
+      default: {
+        // 5 stages (80 KB of LDS, two workgroups per CU) unless the grid has
+        // 513 .. 768 tiles: then 3 stages (48 KB, three per CU) run it in one
+        // wave of workgroups instead of two (the QKV projection at 1024 tokens)
+        const int64_t t64 = (int64_t)(a.gw ? a.groups : 1) * ((a.M + 63) / 64) * ((a.N + 63) / 64);
+        if (t64 > 512 && t64 <= 768) return launch_dl<64, 64, 3>(epi, a, s);
+        return launch_dl<64, 64, 5>(epi, a, s);
+      }
     }
   }
   return launch_t<float, 64, 64>(epi, a, s);

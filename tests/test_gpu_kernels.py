@@ -59,6 +59,18 @@ def test_gemm_bf16_tiles(tile, epi, M, N, K):
 
 @pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
                                  B.DIT_EPI_STORE_F32])
+@pytest.mark.parametrize("M,N,K", [(1000, 2300, 520), (1000, 2300, 64)])
+def test_gemm_bf16_three_stage_ring(epi, M, N, K):
+    # 64x64 tiles on a grid of 513 .. 768 tiles take the three-stage ring
+    require_gpu()
+    announce("gemm bf16 3-stage", epi, M, N, K)
+    err = _gemm_case("bf16", epi, M, N, K, 3)
+    tol = 5e-3 if epi in (B.DIT_EPI_STORE, B.DIT_EPI_GELU) else 1e-5
+    assert err < tol, err
+
+
+@pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
+                                 B.DIT_EPI_STORE_F32])
 @pytest.mark.parametrize("M,N,K", [(16, 64, 16), (100, 72, 264), (77, 16, 64)])
 def test_gemm_f32(epi, M, N, K):
     require_gpu()
