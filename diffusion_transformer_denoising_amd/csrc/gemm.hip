@@ -642,15 +642,18 @@ bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) 
 
 // Tile choice (measured on MI355X): 256x256 with 8 waves (two per SIMD, 3-15%
 // faster than 4 waves on every large step shape) once the grid has at least
-// half a tile per CU; else 128x128 from half a tile per CU for the plain
-// epilogues (MLP-1 at 1024 tokens, 192 tiles: 3-6 % faster than 64x64) but
+// half a tile per CU; else 64x64 while those tiles fit one wave of
+// workgroups (MLP-1 at 1024 tokens, 768 tiles: 11.0 against 12.0 us for
+// 128x128); else 128x128 from half a tile per CU for the plain epilogues but
 // from one per CU for the split store with RoPE, whose heavier epilogue
 // favours more, smaller tiles; else 64x64.
 static int pick_tile(int M, int N, int groups, Epilogue epi) {
   const int64_t G = groups > 1 ? groups : 1;
   const int64_t t256 = G * ((M + 255) / 256) * ((N + 255) / 256);
   const int64_t t128 = G * ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t t64 = G * ((M + 63) / 64) * ((N + 63) / 64);
   if (t256 >= 128) return 4;
+  if (t64 <= 768) return 3;  // one wave of 64x64 workgroups (two or three per CU)
   if (t128 >= (epi == EPI_SPLIT ? 256 : 128)) return 2;
   return 3;
 }
