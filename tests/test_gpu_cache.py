@@ -209,3 +209,28 @@ def test_cache_call_validation():
     m.denoise_step_cached(X, ctx, 500.0, 0.5, 0.45)
     torch.cuda.synchronize()
     assert m.cache_state()["step"] == 1
+
+
+def test_cached_guided_offloaded_run_matches_oracle():
+    # all three options at once: guided steps, block weights streamed from
+    # host memory, block caching with the pages' knobs (three cached in a row)
+    require_gpu()
+    cfg = workload("image_s_bf16", latent=(1, 8, 12), num_blocks=5)
+    announce("cached guided offloaded loop", cfg.tokens)
+    prm = SP.make_params(cfg)
+    for p in prm["blocks"]:
+        p["co_w"] = storage_round(p["co_w"] * 25.0, cfg.dtype)
+    X0 = SP.make_latents(cfg)
+    E, En = SP.make_ctx(cfg), SP.make_ctx(cfg, seed=3)
+    knobs = dict(PAGES, rdt=float("inf"), max_consecutive=3)
+    sched = _sched(cfg, 10)
+    m = DeviceDiT(cfg, prm, guidance=True, offload=True, cache=True)
+    got = _gpu_run(m, X0, dev_tensor(E, cfg.dtype), sched, knobs, dev_tensor(En, cfg.dtype), 4.0)
+    m.close()
+    hits = [h for _, _, h, _ in got]
+    assert sum(hits) >= 3
+    ref = sample_cached(X0, [E, En], prm, cfg, CacheKnobs(**knobs), sched, 4.0, force=hits)
+    tol = tolerances(cfg)
+    for (Xg, Vg, _, _), (Xo, Vo, _, _) in zip(got, ref):
+        assert rel_l2(Vg, Vo) < tol["velocity"]
+        assert rel_l2(Xg, Xo) < tol["latents"]
