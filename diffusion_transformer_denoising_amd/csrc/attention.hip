@@ -706,12 +706,15 @@ static hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
   const int64_t problems = (int64_t)a.heads * (a.batch > 1 ? a.batch : 1);
   while (nw > 1 && (int64_t)((a.sq + 32 * nw - 1) / (32 * nw)) * problems < 128) nw >>= 1;
   dim3 grid((a.sq + 32 * nw - 1) / (32 * nw), a.heads, a.batch > 1 ? a.batch : 1);
-  // Small grids (at most two waves per workgroup): split the keys in two
-  // ranges, each covered by its own set of waves for the same queries, so the
-  // workgroup runs twice the waves and every SIMD of its CU has work.  Needs
-  // at least two key tiles.
-  if (nw <= 2 && a.sk > ATT_BK) {
-    if (nw == 2)
+  // Small grids (fewer waves in all than two per SIMD of the chip): split the
+  // keys in two ranges, each covered by its own set of waves for the same
+  // queries, so every workgroup runs twice the waves.  Needs at least two key
+  // tiles.
+  const int64_t waves = (int64_t)grid.x * grid.y * grid.z * nw;
+  if (nw <= 4 && waves < 2048 && a.sk > ATT_BK) {
+    if (nw == 4)
+      attention_bf16_kernel<HD, 8, 2><<<grid, 512, 0, s>>>(a);
+    else if (nw == 2)
       attention_bf16_kernel<HD, 4, 2><<<grid, 256, 0, s>>>(a);
     else
       attention_bf16_kernel<HD, 2, 2><<<grid, 128, 0, s>>>(a);
