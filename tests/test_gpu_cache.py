@@ -234,3 +234,30 @@ def test_cached_guided_offloaded_run_matches_oracle():
     for (Xg, Vg, _, _), (Xo, Vo, _, _) in zip(got, ref):
         assert rel_l2(Vg, Vo) < tol["velocity"]
         assert rel_l2(Xg, Xo) < tol["latents"]
+
+
+def test_plain_steps_between_cached_steps_leave_the_run_alone():
+    # the cached residuals live in their own part of the workspace: plain and
+    # guided-free steps on the same handle between the steps of a cached run
+    # must not change the run (bitwise, same launches on the same values)
+    require_gpu()
+    cfg = workload("image_s_bf16", latent=(1, 8, 12), num_blocks=4)
+    announce("cached run with plain steps interleaved", cfg.tokens)
+    prm = SP.make_params(cfg)
+    X0 = SP.make_latents(cfg)
+    ctx = dev_tensor(SP.make_ctx(cfg), cfg.dtype)
+    other = dev_tensor(SP.make_ctx(cfg, seed=7), cfg.dtype)
+    sched = _sched(cfg, 8)
+    knobs = dict(PAGES, warmup=2, rdt=float("inf"), max_consecutive=2)
+    m = DeviceDiT(cfg, prm, cache=True)
+    ref = _gpu_run(m, X0, ctx, sched, knobs)
+    m.cache_begin(**knobs)
+    X = torch.from_numpy(X0).cuda()
+    Y = torch.from_numpy(X0[::-1].copy()).cuda()
+    v = torch.empty_like(X)
+    for i, (t, s0, s1) in enumerate(sched):
+        m.denoise_step(Y, other, 300.0, 0.3, 0.25)          # unrelated plain step
+        m.denoise_step_cached(X, ctx, t, s0, s1, v_out=v)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(X), ref[i][0]) and np.array_equal(to_np(v), ref[i][1]), i
+        assert bool(m.cache_state()["hit"]) == ref[i][2]
