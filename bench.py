@@ -25,9 +25,9 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                  torch.cuda.synchronize(), HIP events on the launch stream)
   roofline       the kernel kind with the largest share of step time: its
                  algorithmic FLOPs (or bytes) per launch over its average launch
-                 duration, from HIP events recorded around every launch during a
-                 second pass over the same K steps (less the time of an empty
-                 event pair on the same stream), against the MI355X peak;
+                 duration, from HIP events attached to every launch (recorded at
+                 the kernel's own dispatch and completion) during a second pass
+                 over the same K steps, against the MI355X peak;
                  traffic = HBM bytes per launch from committed rocprofv3
                  FETCH_SIZE / WRITE_SIZE runs (profiles/traffic.json), or null
   attention / gemm   TFLOP/s and fraction of the bf16 MFMA peak, same events
@@ -249,7 +249,7 @@ def main(argv=None) -> int:
     timed_hits = hits[0]
     log(f"[bench] {args.steps} steps: {ms:.2f} ms (events), {wall * 1e3:.2f} ms (wall)")
 
-    # second pass over the same K steps with every launch bracketed by events
+    # second pass over the same K steps with events attached to every launch
     B.dit_profile_enable(m.handle, True)
     run(args.steps)
     torch.cuda.synchronize()
@@ -276,22 +276,10 @@ def main(argv=None) -> int:
     peak = PEAK_TFLOPS[cfg.dtype]
     att_tf, gemm_tf = group_rate(ATTN_KINDS), group_rate(GEMM_KINDS)
 
-    # An event pair recorded around a launch also times the two markers; an
-    # empty pair on the same stream measures that overhead, which is taken off
-    # the bracketed average of the roofline kernel.
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(200)]
-    for a0, a1 in pairs:
-        a0.record(stream)
-        a1.record(stream)
-    torch.cuda.synchronize()
-    overhead_ms = float(np.median([a0.elapsed_time(a1) for a0, a1 in pairs]))
-
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     unit, amount = work[dom]
     n_dom, ms_dom = prof[dom]
-    avg_raw = ms_dom / n_dom / 1e3
-    avg = max(avg_raw - overhead_ms / 1e3, 0.5 * avg_raw)
+    avg = ms_dom / n_dom / 1e3
     src = "attention.hip" if dom.startswith("attention") else (
         "gemm.hip" if dom.startswith("gemm") else "pointwise.hip")
     if unit == "flop":
@@ -304,8 +292,10 @@ def main(argv=None) -> int:
     roof["traffic"] = measured_traffic(dom, cfg.name)
     roof["kernel"] = dom
     roof["per_launch"] = {"work": amount, "work_unit": "FLOP" if unit == "flop" else "byte",
-                          "avg_us": round(avg * 1e6, 3), "avg_us_bracketed": round(avg_raw * 1e6, 3),
-                          "event_pair_overhead_us": round(overhead_ms * 1e3, 3), "source": src}
+                          "avg_us": round(avg * 1e6, 3), "launches": n_dom,
+                          "timing": "start/stop events attached to each launch "
+                                    "(hipExtLaunchKernelGGL), launch stream",
+                          "source": src}
 
     fl = cfg.flops_per_step()
     if guided:

@@ -20,6 +20,13 @@
 
 using namespace dit;
 
+namespace dit {
+LaunchTiming &launch_timing() {
+  static thread_local LaunchTiming t;
+  return t;
+}
+}  // namespace dit
+
 namespace {
 
 constexpr size_t WS_ALIGN = 256;
@@ -174,20 +181,27 @@ dit_status hip_status(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_
     if (_e != hipSuccess) return DIT_ERR_HIP; \
   } while (0)
 
-// Launch `expr` on stream s; with profiling on, bracket it with two events.
+// Launch `expr` (one kernel) on stream s; with profiling on, its launch
+// records two events at the kernel's own start and end (dit_launch).  A
+// launcher that enqueued no kernel leaves them pending: they are then
+// recorded back to back, a zero-length interval.
 #define DIT_RUN(m, kind, s, expr)                                        \
   do {                                                                   \
-    hipEvent_t _e0 = nullptr, _e1 = nullptr;                             \
     if ((m)->prof.on) {                                                  \
-      _e0 = (m)->prof.get();                                             \
-      _e1 = (m)->prof.get();                                             \
+      hipEvent_t _e0 = (m)->prof.get(), _e1 = (m)->prof.get();           \
       if (!_e0 || !_e1) return DIT_ERR_HIP;                              \
-      DIT_TRY(hipEventRecord(_e0, s));                                   \
-    }                                                                    \
-    DIT_TRY(expr);                                                       \
-    if ((m)->prof.on) {                                                  \
-      DIT_TRY(hipEventRecord(_e1, s));                                   \
+      launch_timing() = LaunchTiming{_e0, _e1};                          \
+      const hipError_t _r = (expr);                                      \
+      const bool _pending = launch_timing().start != nullptr;            \
+      launch_timing() = LaunchTiming{};                                  \
+      DIT_TRY(_r);                                                       \
+      if (_pending) {                                                    \
+        DIT_TRY(hipEventRecord(_e0, s));                                 \
+        DIT_TRY(hipEventRecord(_e1, s));                                 \
+      }                                                                  \
       (m)->prof.recs.push_back({(int)(kind), (m)->prof.next - 2});       \
+    } else {                                                             \
+      DIT_TRY(expr);                                                     \
     }                                                                    \
   } while (0)
 

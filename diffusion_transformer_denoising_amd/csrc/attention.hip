@@ -713,25 +713,25 @@ static hipError_t launch_attn_bf16(const AttnArgs &a, hipStream_t s) {
   const int64_t waves = (int64_t)grid.x * grid.y * grid.z * nw;
   if (nw <= 4 && waves < 2048 && a.sk > ATT_BK) {
     if (nw == 4)
-      attention_bf16_kernel<HD, 8, 2><<<grid, 512, 0, s>>>(a);
+      dit_launch(attention_bf16_kernel<HD, 8, 2>, grid, 512, s, a);
     else if (nw == 2)
-      attention_bf16_kernel<HD, 4, 2><<<grid, 256, 0, s>>>(a);
+      dit_launch(attention_bf16_kernel<HD, 4, 2>, grid, 256, s, a);
     else
-      attention_bf16_kernel<HD, 2, 2><<<grid, 128, 0, s>>>(a);
+      dit_launch(attention_bf16_kernel<HD, 2, 2>, grid, 128, s, a);
     return hipGetLastError();
   }
   if constexpr (MAXNW == 8) {
     if (nw == 8) {
-      attention_bf16_kernel<HD, 8><<<grid, 512, 0, s>>>(a);
+      dit_launch(attention_bf16_kernel<HD, 8>, grid, 512, s, a);
       return hipGetLastError();
     }
   }
   if (nw == 4)
-    attention_bf16_kernel<HD, 4><<<grid, 256, 0, s>>>(a);
+    dit_launch(attention_bf16_kernel<HD, 4>, grid, 256, s, a);
   else if (nw == 2)
-    attention_bf16_kernel<HD, 2><<<grid, 128, 0, s>>>(a);
+    dit_launch(attention_bf16_kernel<HD, 2>, grid, 128, s, a);
   else
-    attention_bf16_kernel<HD, 1><<<grid, 64, 0, s>>>(a);
+    dit_launch(attention_bf16_kernel<HD, 1>, grid, 64, s, a);
   return hipGetLastError();
 }
 
@@ -739,9 +739,9 @@ template <typename T>
 static hipError_t launch_attn_t(const AttnArgs &a, hipStream_t s) {
   dim3 grid((a.sq + ATT_BQ - 1) / ATT_BQ, a.heads, a.batch > 1 ? a.batch : 1);
   switch (a.head_dim) {
-    case 32: attention_kernel<T, 32><<<grid, 256, 0, s>>>(a); break;
-    case 64: attention_kernel<T, 64><<<grid, 256, 0, s>>>(a); break;
-    case 128: attention_kernel<T, 128><<<grid, 256, 0, s>>>(a); break;
+    case 32: dit_launch(attention_kernel<T, 32>, grid, 256, s, a); break;
+    case 64: dit_launch(attention_kernel<T, 64>, grid, 256, s, a); break;
+    case 128: dit_launch(attention_kernel<T, 128>, grid, 256, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

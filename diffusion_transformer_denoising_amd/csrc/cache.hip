@@ -65,7 +65,7 @@ int cache_probe_groups(int64_t n) {
 hipError_t launch_cache_probe(const float *x, float *h0, float *probe, const float *ref, int64_t n,
                               double *partials, hipStream_t s) {
   if (n <= 0 || (n & 3)) return hipErrorInvalidValue;
-  cache_probe_kernel<<<cache_probe_groups(n), 256, 0, s>>>(x, h0, probe, ref, n / 4, partials);
+  dit_launch(cache_probe_kernel, cache_probe_groups(n), 256, s, x, h0, probe, ref, n / 4, partials);
   return hipGetLastError();
 }
 
@@ -98,7 +98,7 @@ hipError_t launch_cache_apply(float *x, const float *tf, int64_t n, int nf, floa
                               hipStream_t s) {
   if (n <= 0 || (n & 3) || nf < 1 || nf > 3) return hipErrorInvalidValue;
   const int64_t threads = n / 4;
-  cache_apply_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(x, tf, n, nf, c1, c2);
+  dit_launch(cache_apply_kernel, (unsigned)((threads + 255) / 256), 256, s, x, tf, n, nf, c1, c2);
   return hipGetLastError();
 }
 
@@ -131,7 +131,7 @@ hipError_t launch_cache_update(const float *x, const float *hf, float *tf, int64
                                float gap, hipStream_t s) {
   if (n <= 0 || (n & 3) || nnew < 1 || nnew > 3 || !(gap >= 1.0f)) return hipErrorInvalidValue;
   const int64_t threads = n / 4;
-  cache_update_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(x, hf, tf, n, nnew, gap);
+  dit_launch(cache_update_kernel, (unsigned)((threads + 255) / 256), 256, s, x, hf, tf, n, nnew, gap);
   return hipGetLastError();
 }
 

@@ -610,11 +610,11 @@ static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
   dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM), a.gw ? a.groups : 1);
   constexpr int NT = 64 * NW;
   switch (epi) {
-    case EPI_STORE: gemm_kernel<T, BM, BN, EPI_STORE, NWN, NW><<<grid, NT, 0, s>>>(a); break;
-    case EPI_GELU: gemm_kernel<T, BM, BN, EPI_GELU, NWN, NW><<<grid, NT, 0, s>>>(a); break;
-    case EPI_RESIDUAL: gemm_kernel<T, BM, BN, EPI_RESIDUAL, NWN, NW><<<grid, NT, 0, s>>>(a); break;
-    case EPI_STORE_F32: gemm_kernel<T, BM, BN, EPI_STORE_F32, NWN, NW><<<grid, NT, 0, s>>>(a); break;
-    case EPI_SPLIT: gemm_kernel<T, BM, BN, EPI_SPLIT, NWN, NW><<<grid, NT, 0, s>>>(a); break;
+    case EPI_STORE: dit_launch(gemm_kernel<T, BM, BN, EPI_STORE, NWN, NW>, grid, NT, s, a); break;
+    case EPI_GELU: dit_launch(gemm_kernel<T, BM, BN, EPI_GELU, NWN, NW>, grid, NT, s, a); break;
+    case EPI_RESIDUAL: dit_launch(gemm_kernel<T, BM, BN, EPI_RESIDUAL, NWN, NW>, grid, NT, s, a); break;
+    case EPI_STORE_F32: dit_launch(gemm_kernel<T, BM, BN, EPI_STORE_F32, NWN, NW>, grid, NT, s, a); break;
+    case EPI_SPLIT: dit_launch(gemm_kernel<T, BM, BN, EPI_SPLIT, NWN, NW>, grid, NT, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -624,11 +624,11 @@ template <int BM, int BN, int NS>
 static hipError_t launch_dl(Epilogue epi, const GemmArgs &a, hipStream_t s) {
   dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM), a.gw ? a.groups : 1);
   switch (epi) {
-    case EPI_STORE: gemm_dl_kernel<BM, BN, NS, EPI_STORE><<<grid, 256, 0, s>>>(a); break;
-    case EPI_GELU: gemm_dl_kernel<BM, BN, NS, EPI_GELU><<<grid, 256, 0, s>>>(a); break;
-    case EPI_RESIDUAL: gemm_dl_kernel<BM, BN, NS, EPI_RESIDUAL><<<grid, 256, 0, s>>>(a); break;
-    case EPI_STORE_F32: gemm_dl_kernel<BM, BN, NS, EPI_STORE_F32><<<grid, 256, 0, s>>>(a); break;
-    case EPI_SPLIT: gemm_dl_kernel<BM, BN, NS, EPI_SPLIT><<<grid, 256, 0, s>>>(a); break;
+    case EPI_STORE: dit_launch(gemm_dl_kernel<BM, BN, NS, EPI_STORE>, grid, 256, s, a); break;
+    case EPI_GELU: dit_launch(gemm_dl_kernel<BM, BN, NS, EPI_GELU>, grid, 256, s, a); break;
+    case EPI_RESIDUAL: dit_launch(gemm_dl_kernel<BM, BN, NS, EPI_RESIDUAL>, grid, 256, s, a); break;
+    case EPI_STORE_F32: dit_launch(gemm_dl_kernel<BM, BN, NS, EPI_STORE_F32>, grid, 256, s, a); break;
+    case EPI_SPLIT: dit_launch(gemm_dl_kernel<BM, BN, NS, EPI_SPLIT>, grid, 256, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

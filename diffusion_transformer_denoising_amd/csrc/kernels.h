@@ -1,10 +1,33 @@
 // kernels.h -- host-side launchers of the DiT kernels (internal to libdit.so).
 // Every launcher validates nothing: the C ABI layer checks shapes first.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace dit {
+
+// Kernel launches.  When a start event is pending in launch_timing() (the
+// profiler sets one before a timed launch), the next dit_launch records it at
+// the kernel's own dispatch and the stop event at its completion, through
+// hipExtLaunchKernelGGL, rather than as two separate commands around it;
+// otherwise it is a plain launch.
+struct LaunchTiming {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTiming &launch_timing();  // per host thread
+
+template <typename F, typename... Args>
+inline void dit_launch(F kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  LaunchTiming &t = launch_timing();
+  if (t.start) {
+    const hipEvent_t a = t.start, b = t.stop;
+    t = LaunchTiming{};
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+}
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
 

@@ -80,7 +80,7 @@ template <typename T, int NV = 1>
 static void launch_ln_t(int nvl, dim3 grid, hipStream_t s, const float *x, int rows, int D, float eps,
                         const float *shift, const float *scale, T *y) {
   if (nvl == NV) {
-    ln_mod_kernel<T, NV><<<grid, 256, 0, s>>>(x, rows, D, eps, shift, scale, y);
+    dit_launch(ln_mod_kernel<T, NV>, grid, 256, s, x, rows, D, eps, shift, scale, y);
   } else if constexpr (NV < LN_MAXV) {
     launch_ln_t<T, NV + 1>(nvl, grid, s, x, rows, D, eps, shift, scale, y);
   }
@@ -132,7 +132,7 @@ hipError_t launch_rope_tables(float *cos_t, float *sin_t, int gf, int gh, int gw
   const int64_t total = (int64_t)gf * gh * gw * (head_dim / 2);
   if (total <= 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
-  rope_table_kernel<<<grid, 256, 0, s>>>(cos_t, sin_t, gf, gh, gw, head_dim / 2, rf, rh, rw,
+  dit_launch(rope_table_kernel, grid, 256, s, cos_t, sin_t, gf, gh, gw, head_dim / 2, rf, rh, rw,
                                          (double)theta);
   return hipGetLastError();
 }
@@ -164,10 +164,10 @@ hipError_t launch_patchify(DType dt, const float *X, void *patches, int C, int F
   if (total <= 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
   if (dt == DT_BF16)
-    patchify_kernel<bf16><<<grid, 256, 0, s>>>(X, static_cast<bf16 *>(patches), C, F, H, W, pf,
+    dit_launch(patchify_kernel<bf16>, grid, 256, s, X, static_cast<bf16 *>(patches), C, F, H, W, pf,
                                                ph, pw);
   else
-    patchify_kernel<float><<<grid, 256, 0, s>>>(X, static_cast<float *>(patches), C, F, H, W, pf,
+    dit_launch(patchify_kernel<float>, grid, 256, s, X, static_cast<float *>(patches), C, F, H, W, pf,
                                                 ph, pw);
   return hipGetLastError();
 }
@@ -213,7 +213,7 @@ hipError_t launch_unpatchify_euler(const float *u, const float *u_neg, float g, 
   const int64_t total = (int64_t)C * F * H * W;
   if (total <= 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
-  unpatchify_euler_kernel<<<grid, 256, 0, s>>>(u, u_neg, g, X, v_out, dt, C, F, H, W, pf, ph, pw);
+  dit_launch(unpatchify_euler_kernel, grid, 256, s, u, u_neg, g, X, v_out, dt, C, F, H, W, pf, ph, pw);
   return hipGetLastError();
 }
 
@@ -236,7 +236,7 @@ hipError_t launch_euler(float *X, const float *v, int64_t n, float dt, hipStream
   if (n <= 0) return hipSuccess;
   const int64_t threads = (n + 3) / 4;
   dim3 grid((unsigned)((threads + 255) / 256));
-  euler_kernel<<<grid, 256, 0, s>>>(X, v, n, dt);
+  dit_launch(euler_kernel, grid, 256, s, X, v, n, dt);
   return hipGetLastError();
 }
 
@@ -294,10 +294,10 @@ hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, f
   if (K > GEMV_MAXK || (!x && (K & 1)) || (nfan > 0 && (!fan || !fan_out))) return hipErrorInvalidValue;
   dim3 grid((N + 3) / 4);
   if (dt == DT_BF16)
-    gemv_kernel<bf16><<<grid, 256, 0, s>>>(static_cast<const bf16 *>(W), static_cast<const bf16 *>(b),
+    dit_launch(gemv_kernel<bf16>, grid, 256, s, static_cast<const bf16 *>(W), static_cast<const bf16 *>(b),
                                            x, (double)t, y, N, K, silu_in, fan, nfan, fan_out);
   else
-    gemv_kernel<float><<<grid, 256, 0, s>>>(static_cast<const float *>(W), static_cast<const float *>(b),
+    dit_launch(gemv_kernel<float>, grid, 256, s, static_cast<const float *>(W), static_cast<const float *>(b),
                                             x, (double)t, y, N, K, silu_in, fan, nfan, fan_out);
   return hipGetLastError();
 }

@@ -327,8 +327,9 @@ dit_status dit_time_embedding(dit_model *model, float t, float *block_mod, float
                               float *temb, void *stream);
 
 /* Per-launch timing (diagnostics).  While enabled on a handle, every kernel
- * launch of dit_block_forward / dit_denoise_step / dit_time_embedding is
- * bracketed by two HIP events recorded on the call's stream.  Enabling clears
+ * launch of the handle's calls (blocks, steps, time embedding) carries two
+ * HIP events that the runtime records at the kernel's own dispatch and
+ * completion on the call's stream (extended launch).  Enabling clears
  * earlier records; disabling keeps them for reading.  dit_profile_read waits
  * for the recorded events of one kind and returns the number of launches and
  * their summed duration in milliseconds.  Kinds are 0 .. dit_profile_kind_count()-1,
