@@ -19,7 +19,7 @@
 //     directly (buffer loads with the LDS destination) into a ring of NS
 //     stages, so NS-1 slices are in flight; small problems have too few
 //     workgroups per CU to hide memory latency any other way.
-// Both share the LDS-staged epilogue (gemm_epilogue).
+// Both share the LDS-staged epilogue (GemmEpilogue).
 #include "device.h"
 #include "kernels.h"
 
@@ -68,8 +68,14 @@ __device__ __forceinline__ void wave_lds_sync() {
 // for it) rotates the (2j, 2j+1) pairs of a run in fp32 before rounding.  A
 // transposed segment goes through a transposed strip, so each output row
 // (one column of C) gets 16-byte runs of consecutive tokens.
-// The caller has synchronised the workgroup: scratch is free LDS of at least
-// 4 * gemm_strip_floats<...>() floats.
+// The global operands of a lane (bias and gate of its columns; residual x or
+// RoPE cos / sin of its runs) are read either strip by strip inside the
+// epilogue or, with PRE, all at once by prefetch() before the main loop, so
+// that their memory latency is spent under the products instead of after the
+// last one (it is a visible part of a short-K problem; PRE costs registers,
+// which the small tiles have to spare).  Every output element has one owner,
+// and the residual stream is never an operand of its own product, so reading
+// it early reads the same values.
 // ---------------------------------------------------------------------------
 template <typename T, int WN>
 constexpr int gemm_strip_floats() {
@@ -79,187 +85,243 @@ constexpr int gemm_strip_floats() {
 
 // NWN waves along N, NW waves in all (NW / NWN along M); each wave owns a
 // WM x WN block as TM x TN 32x32 accumulators.
-template <typename T, int BM, int BN, int EPI, int NWN = 2, int NW = 4>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs &p,
-                                              f32x16 (&acc)[BM * NWN / NW / 32][BN / NWN / 32],
-                                              float *scratch, int m0, int n0, const void *bias_g,
-                                              int g) {
-  constexpr int WM = BM * NWN / NW, WN = BN / NWN, TM = WM / 32, TN = WN / 32;
-  constexpr int SROW = WN + 4;                        // fp32 strip row stride
-  constexpr int TROW = 32 + 16 / (int)sizeof(T);      // transposed strip row stride
-  constexpr int REG = gemm_strip_floats<T, WN>();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / NWN, wn = wave % NWN;
-  const int M = p.M, N = p.N;
-  float *strip = scratch + wave * REG;
-  T *stripT = reinterpret_cast<T *>(strip);
-  const T *bias = static_cast<const T *>(bias_g);
-  const int colbase = n0 + wn * WN;
-  int segc = colbase, trans = 0, rope = 0;
-  void *dst = p.out;
-  int64_t ld = p.ldo;
-  if constexpr (EPI == EPI_SPLIT) {
-    const int seg = colbase / p.seg_width;  // a strip never straddles segments
-    segc = colbase - seg * p.seg_width;
-    trans = p.seg_trans[seg];
-    rope = p.seg_rope[seg];
-    dst = static_cast<T *>(p.seg_ptr[seg]) + (int64_t)g * p.seg_gstride[seg];
-    ld = p.seg_ld[seg];
-  }
-  constexpr int VE = EPI == EPI_RESIDUAL || EPI == EPI_STORE_F32 || sizeof(T) == 4 ? 4 : 8;
-  const bool vec_ok = (ld % VE) == 0;
+template <typename T, int BM, int BN, int EPI, int NWN = 2, int NW = 4, bool PRE = false>
+struct GemmEpilogue {
+  static constexpr int WM = BM * NWN / NW, WN = BN / NWN, TM = WM / 32, TN = WN / 32;
+  static constexpr int SROW = WN + 4;                        // fp32 strip row stride
+  static constexpr int TROW = 32 + 16 / (int)sizeof(T);      // transposed strip row stride
+  static constexpr int REG = gemm_strip_floats<T, WN>();
+  static constexpr int UPR = WN / 8;                         // 8-column runs per strip row
+  static constexpr int NIT = 32 * UPR / 64;                  // runs per lane per strip
+  static_assert((32 * UPR) % 64 == 0, "whole runs per lane");
+  static constexpr int VE = EPI == EPI_RESIDUAL || EPI == EPI_STORE_F32 || sizeof(T) == 4 ? 4 : 8;
 
-#pragma unroll
-  for (int a = 0; a < TM; ++a) {
-    const int rowbase = m0 + wm * WM + a * 32;
-    // 1. accumulators -> strip
+  const GemmArgs &p;
+  const T *bias;
+  int lane, wave, wm, M, N, m0, colbase, segc, trans, rope;
+  void *dst;
+  int64_t ld;
+  bool vec_ok;
+  uint32_t bw[TN];  // bias bits (bf16 in the low half, or fp32) until used
+  float gv[TN];
+  f32x4 pre[PRE ? TM : 1][NIT][2];  // per strip with PRE, else the current strip's
+
+  __device__ __forceinline__ GemmEpilogue(const GemmArgs &args, int m0_, int n0,
+                                          const void *bias_g, int g)
+      : p(args), bias(static_cast<const T *>(bias_g)) {
+    lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar segment lookups
+    wm = wave / NWN;
+    M = p.M;
+    N = p.N;
+    m0 = m0_;
+    colbase = n0 + (wave % NWN) * WN;
+    segc = colbase;
+    trans = 0;
+    rope = 0;
+    dst = p.out;
+    ld = p.ldo;
+    if constexpr (EPI == EPI_SPLIT) {
+      const int seg = colbase / p.seg_width;  // a strip never straddles segments
+      segc = colbase - seg * p.seg_width;
+      trans = p.seg_trans[seg];
+      rope = p.seg_rope[seg];
+      dst = static_cast<T *>(p.seg_ptr[seg]) + (int64_t)g * p.seg_gstride[seg];
+      ld = p.seg_ld[seg];
+    }
+    vec_ok = (ld % VE) == 0;
+  }
+
+  // bias and gate of the lane's column in each 32-column block, by raw buffer
+  // loads: past column N, and for a missing operand (an empty range), they
+  // return zero without a branch; the bias stays raw bits until it is used, so
+  // nothing waits for these loads where they are issued
+  __device__ __forceinline__ void load_cols() {
+    const auto br = make_rsrc(bias ? static_cast<const void *>(bias) : p.A,
+                              bias ? (uint32_t)(N * sizeof(T)) : 0u);
+    const auto gr = make_rsrc(EPI == EPI_RESIDUAL && p.gate ? static_cast<const void *>(p.gate) : p.A,
+                              EPI == EPI_RESIDUAL && p.gate ? (uint32_t)(N * 4) : 0u);
 #pragma unroll
     for (int b = 0; b < TN; ++b) {
-      const int sc = b * 32 + (lane & 31);
-      const int col = colbase + sc;
-      const float bv = (bias && col < N) ? to_f32(bias[col]) : 0.0f;
-      float gv = 1.0f;
-      if constexpr (EPI == EPI_RESIDUAL) gv = (p.gate && col < N) ? p.gate[col] : 1.0f;
+      const uint32_t col = (uint32_t)(colbase + b * 32 + (lane & 31));
+      if constexpr (sizeof(T) == 2)
+        bw[b] = __builtin_amdgcn_raw_buffer_load_b16(br, col * 2, 0, 0);
+      else
+        bw[b] = __builtin_amdgcn_raw_buffer_load_b32(br, col * 4, 0, 0);
+      gv[b] = 1.0f;
+      if constexpr (EPI == EPI_RESIDUAL)
+        gv[b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gr, col * 4, 0, 0));
+    }
+  }
+
+  // residual x (or RoPE cos / sin) of the lane's runs in strip a; runs that
+  // take the scalar path (ragged N, unaligned ld) read nothing here
+  __device__ __forceinline__ void load_runs(int a, f32x4 (&r)[NIT][2]) {
+    if constexpr (EPI == EPI_RESIDUAL || EPI == EPI_SPLIT) {
+      if (EPI == EPI_SPLIT && (trans || !rope)) return;
+      const int rowbase = m0 + wm * WM + a * 32;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r0 = j * 8 + (lane >> 5) * 4;
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = acc[a][b][j * 4 + i] + bv;
-          if constexpr (EPI == EPI_GELU) v[i] = gelu_tanh(v[i]);
-          if constexpr (EPI == EPI_RESIDUAL) v[i] *= gv;
-        }
-        if (EPI == EPI_SPLIT && trans) {
-          if constexpr (sizeof(T) == 2) {
-            bf16x4 t4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t4[i] = (bf16)v[i];
-            *reinterpret_cast<bf16x4 *>(stripT + sc * TROW + r0) = t4;
-          } else {
-            *reinterpret_cast<f32x4 *>(stripT + sc * TROW + r0) = f32x4{v[0], v[1], v[2], v[3]};
+      for (int it = 0; it < NIT; ++it) {
+        const int u = lane + it * 64;
+        const int rr = u / UPR, c8 = (u % UPR) * 8;
+        const int row = rowbase + rr, col = colbase + c8;
+        if (row >= M || col >= N) continue;
+        if constexpr (EPI == EPI_RESIDUAL) {
+          if (vec_ok && N - col >= 8) {
+            const float *o = static_cast<const float *>(dst) + (int64_t)row * ld + col;
+            r[it][0] = *reinterpret_cast<const f32x4 *>(o);
+            r[it][1] = *reinterpret_cast<const f32x4 *>(o + 4);
           }
         } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) strip[(r0 + i) * SROW + sc] = v[i];
+          // pairs (2j, 2j+1) of the head; table column = channel / 2
+          const int ch0 = (segc + c8) % (2 * p.rope_half_d);
+          const int trow = p.seg_rows > 0 ? row % p.seg_rows : row;  // token position
+          const int64_t t = (int64_t)trow * p.rope_half_d + ch0 / 2;
+          r[it][0] = *reinterpret_cast<const f32x4 *>(p.rope_cos + t);
+          r[it][1] = *reinterpret_cast<const f32x4 *>(p.rope_sin + t);
         }
       }
     }
-    wave_lds_sync();
-    // 2. strip -> global, 8-element runs
-    if (EPI == EPI_SPLIT && trans) {
-      // row c of the transposed strip = column segc + c of C = output row
-      for (int u = lane; u < WN * 4; u += 64) {
-        const int c = u >> 2, rr = (u & 3) * 8;
-        const int row = rowbase + rr;
-        if (row >= M) continue;  // runs past M stay inside the padded rows
-        // stacked sequences: token row % seg_rows of sequence row / seg_rows
-        // (a run of 8 never straddles two: seg_rows is a multiple of 8)
-        const int64_t tcol = p.seg_rows > 0
-                                 ? (int64_t)(row / p.seg_rows) * p.seg_bstride + row % p.seg_rows
-                                 : row;
-        T *o = static_cast<T *>(dst) + (int64_t)(segc + c) * ld + tcol;
-        const T *srcp = stripT + c * TROW + rr;
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<U128 *>(o) = *reinterpret_cast<const U128 *>(srcp);
-        } else {
-          *reinterpret_cast<f32x4 *>(o) = *reinterpret_cast<const f32x4 *>(srcp);
-          *reinterpret_cast<f32x4 *>(o + 4) = *reinterpret_cast<const f32x4 *>(srcp + 4);
+  }
+
+  __device__ __forceinline__ void prefetch() {
+    static_assert(PRE, "prefetch() belongs to the PRE form");
+    load_cols();
+#pragma unroll
+    for (int a = 0; a < TM; ++a) load_runs(a, pre[a]);
+  }
+
+  // The caller has synchronised the workgroup: scratch is free LDS of at
+  // least NW * REG floats.
+  __device__ __forceinline__ void store(f32x16 (&acc)[TM][TN], float *scratch) {
+    float *strip = scratch + wave * REG;
+    T *stripT = reinterpret_cast<T *>(strip);
+    if constexpr (!PRE) load_cols();
+#pragma unroll
+    for (int a = 0; a < TM; ++a) {
+      const int rowbase = m0 + wm * WM + a * 32;
+      // 1. accumulators -> strip
+#pragma unroll
+      for (int b = 0; b < TN; ++b) {
+        const int sc = b * 32 + (lane & 31);
+        const float bv = __uint_as_float(sizeof(T) == 2 ? bw[b] << 16 : bw[b]);
+        const float gb = EPI == EPI_RESIDUAL && p.gate ? gv[b] : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r0 = j * 8 + (lane >> 5) * 4;
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = acc[a][b][j * 4 + i] + bv;
+            if constexpr (EPI == EPI_GELU) v[i] = gelu_tanh(v[i]);
+            if constexpr (EPI == EPI_RESIDUAL) v[i] *= gb;
+          }
+          if (EPI == EPI_SPLIT && trans) {
+            if constexpr (sizeof(T) == 2) {
+              bf16x4 t4;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) t4[i] = (bf16)v[i];
+              *reinterpret_cast<bf16x4 *>(stripT + sc * TROW + r0) = t4;
+            } else {
+              *reinterpret_cast<f32x4 *>(stripT + sc * TROW + r0) = f32x4{v[0], v[1], v[2], v[3]};
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) strip[(r0 + i) * SROW + sc] = v[i];
+          }
         }
       }
-    } else {
-      constexpr int UPR = WN / 8;              // 8-column runs per strip row
-      constexpr int NIT = 32 * UPR / 64;       // runs per lane
-      static_assert((32 * UPR) % 64 == 0, "whole runs per lane");
-      // First every global read of this lane's runs (the residual x, the RoPE
-      // table entries), then the stores: with a read and a store per run the
-      // compiler cannot move the next run's read above the store (they may
-      // alias), and each run would wait a full memory latency.
-      f32x4 pre[NIT][2];
-      if constexpr (EPI == EPI_RESIDUAL || EPI == EPI_SPLIT) {
+      wave_lds_sync();
+      // 2. strip -> global, 8-element runs
+      if (EPI == EPI_SPLIT && trans) {
+        // row c of the transposed strip = column segc + c of C = output row
+        for (int u = lane; u < WN * 4; u += 64) {
+          const int c = u >> 2, rr = (u & 3) * 8;
+          const int row = rowbase + rr;
+          if (row >= M) continue;  // runs past M stay inside the padded rows
+          // stacked sequences: token row % seg_rows of sequence row / seg_rows
+          // (a run of 8 never straddles two: seg_rows is a multiple of 8)
+          const int64_t tcol = p.seg_rows > 0
+                                   ? (int64_t)(row / p.seg_rows) * p.seg_bstride + row % p.seg_rows
+                                   : row;
+          T *o = static_cast<T *>(dst) + (int64_t)(segc + c) * ld + tcol;
+          const T *srcp = stripT + c * TROW + rr;
+          if constexpr (sizeof(T) == 2) {
+            *reinterpret_cast<U128 *>(o) = *reinterpret_cast<const U128 *>(srcp);
+          } else {
+            *reinterpret_cast<f32x4 *>(o) = *reinterpret_cast<const f32x4 *>(srcp);
+            *reinterpret_cast<f32x4 *>(o + 4) = *reinterpret_cast<const f32x4 *>(srcp + 4);
+          }
+        }
+      } else {
+        // Without PRE, every global read of this lane's runs comes first, then
+        // the stores: with a read and a store per run the compiler cannot move
+        // the next run's read above the store (they may alias), and each run
+        // would wait a full memory latency.
+        const int pa = PRE ? a : 0;
+        if constexpr (!PRE) load_runs(a, pre[0]);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const int u = lane + it * 64;
           const int r = u / UPR, c8 = (u % UPR) * 8;
           const int row = rowbase + r, col = colbase + c8;
           if (row >= M || col >= N) continue;
-          if constexpr (EPI == EPI_RESIDUAL) {
-            if (vec_ok && N - col >= 8) {
-              const float *o = static_cast<const float *>(dst) + (int64_t)row * ld + col;
-              pre[it][0] = *reinterpret_cast<const f32x4 *>(o);
-              pre[it][1] = *reinterpret_cast<const f32x4 *>(o + 4);
+          const int ocol = EPI == EPI_SPLIT ? segc + c8 : col;  // column in the destination
+          const float *sp = strip + r * SROW + c8;
+          const f32x4 lo = *reinterpret_cast<const f32x4 *>(sp);
+          const f32x4 hi = *reinterpret_cast<const f32x4 *>(sp + 4);
+          float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          if (EPI == EPI_SPLIT && rope) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float cs = pre[pa][it][0][q], sn = pre[pa][it][1][q];
+              const float u0 = v[2 * q], u1 = v[2 * q + 1];
+              v[2 * q] = u0 * cs - u1 * sn;
+              v[2 * q + 1] = u0 * sn + u1 * cs;
             }
-          } else if (rope) {
-            // pairs (2j, 2j+1) of the head; table column = channel / 2
-            const int ch0 = (segc + c8) % (2 * p.rope_half_d);
-            const int trow = p.seg_rows > 0 ? row % p.seg_rows : row;  // token position
-            const int64_t t = (int64_t)trow * p.rope_half_d + ch0 / 2;
-            pre[it][0] = *reinterpret_cast<const f32x4 *>(p.rope_cos + t);
-            pre[it][1] = *reinterpret_cast<const f32x4 *>(p.rope_sin + t);
           }
-        }
-      }
+          const int nvalid = N - col < 8 ? N - col : 8;
+          if constexpr (EPI == EPI_RESIDUAL) {
+            float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
+            if (vec_ok && nvalid == 8) {
+              f32x4 x0 = pre[pa][it][0], x1 = pre[pa][it][1];
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int u = lane + it * 64;
-        const int r = u / UPR, c8 = (u % UPR) * 8;
-        const int row = rowbase + r, col = colbase + c8;
-        if (row >= M || col >= N) continue;
-        const int ocol = EPI == EPI_SPLIT ? segc + c8 : col;  // column in the destination
-        const float *sp = strip + r * SROW + c8;
-        const f32x4 lo = *reinterpret_cast<const f32x4 *>(sp);
-        const f32x4 hi = *reinterpret_cast<const f32x4 *>(sp + 4);
-        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if (EPI == EPI_SPLIT && rope) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float cs = pre[it][0][q], sn = pre[it][1][q];
-            const float u0 = v[2 * q], u1 = v[2 * q + 1];
-            v[2 * q] = u0 * cs - u1 * sn;
-            v[2 * q + 1] = u0 * sn + u1 * cs;
-          }
-        }
-        const int nvalid = N - col < 8 ? N - col : 8;
-        if constexpr (EPI == EPI_RESIDUAL) {
-          float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
-          if (vec_ok && nvalid == 8) {
-            f32x4 x0 = pre[it][0], x1 = pre[it][1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { x0[e] += v[e]; x1[e] += v[4 + e]; }
-            *reinterpret_cast<f32x4 *>(o) = x0;
-            *reinterpret_cast<f32x4 *>(o + 4) = x1;
-          } else {
-            for (int e = 0; e < nvalid; ++e) o[e] = o[e] + v[e];
-          }
-        } else if constexpr (EPI == EPI_STORE_F32) {
-          float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
-          if (vec_ok && nvalid == 8) {
-            *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
-          } else {
-            for (int e = 0; e < nvalid; ++e) o[e] = v[e];
-          }
-        } else {
-          T *o = static_cast<T *>(dst) + (int64_t)row * ld + ocol;
-          if (vec_ok && nvalid == 8) {
-            if constexpr (sizeof(T) == 2) {
-              bf16x8 t8;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) t8[e] = (bf16)v[e];
-              *reinterpret_cast<bf16x8 *>(o) = t8;
+              for (int e = 0; e < 4; ++e) { x0[e] += v[e]; x1[e] += v[4 + e]; }
+              *reinterpret_cast<f32x4 *>(o) = x0;
+              *reinterpret_cast<f32x4 *>(o + 4) = x1;
             } else {
+              for (int e = 0; e < nvalid; ++e) o[e] = o[e] + v[e];
+            }
+          } else if constexpr (EPI == EPI_STORE_F32) {
+            float *o = static_cast<float *>(dst) + (int64_t)row * ld + ocol;
+            if (vec_ok && nvalid == 8) {
               *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
               *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            } else {
+              for (int e = 0; e < nvalid; ++e) o[e] = v[e];
             }
           } else {
-            for (int e = 0; e < nvalid; ++e) o[e] = from_f32<T>(v[e]);
+            T *o = static_cast<T *>(dst) + (int64_t)row * ld + ocol;
+            if (vec_ok && nvalid == 8) {
+              if constexpr (sizeof(T) == 2) {
+                bf16x8 t8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t8[e] = (bf16)v[e];
+                *reinterpret_cast<bf16x8 *>(o) = t8;
+              } else {
+                *reinterpret_cast<f32x4 *>(o) = f32x4{v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4 *>(o + 4) = f32x4{v[4], v[5], v[6], v[7]};
+              }
+            } else {
+              for (int e = 0; e < nvalid; ++e) o[e] = from_f32<T>(v[e]);
+            }
           }
         }
       }
+      wave_lds_sync();  // the strip is rewritten by the next pass
     }
-    wave_lds_sync();  // the strip is rewritten by the next pass
   }
-}
+};
 
 // Tile of this workgroup.  grid.x is 1-D over tiles; workgroups are dispatched to the
 // 8 XCDs round-robin (id % 8), so id is first mapped to a contiguous range of
@@ -449,8 +511,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(GemmArgs p) {
 
 
   __syncthreads();  // every wave is done with the main-loop buffers
-  gemm_epilogue<T, BM, BN, EPI, NWN, NW>(p, acc, reinterpret_cast<float *>(&lds[0][0]), m0, n0,
-                                          bias_g, g);
+  GemmEpilogue<T, BM, BN, EPI, NWN, NW>(p, m0, n0, bias_g, g)
+      .store(acc, reinterpret_cast<float *>(&lds[0][0]));
 }
 
 // ---------------------------------------------------------------------------
@@ -468,6 +530,7 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   constexpr int IPS = (BM + BN) / 32;            // load instructions per wave per stage
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
   static_assert((NS - 2) * IPS < 64, "vmcnt range");
+  constexpr bool PRE = TM * TN == 1;  // epilogue operands before the main loop (64x64)
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
   static_assert(4 * gemm_strip_floats<bf16, WN>() * 4 <= NS * STAGE, "epilogue strips");
 
@@ -560,8 +623,13 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
 
   // Slices 0 .. NS-2 in flight; slice kt+1's fragments are read during step kt.
   const int KT = (K + BK - 1) / BK;
+  // The epilogue's operands go out right after slice 0: vector memory
+  // operations complete in issue order, so the count below covers both.
+  issue(0, 0);
+  GemmEpilogue<bf16, BM, BN, EPI, 2, 4, PRE> epi(p, m0, n0, bias_g, g);
+  if constexpr (PRE) epi.prefetch();
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) issue(s, s);
+  for (int s = 1; s < NS - 1; ++s) issue(s, s);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * IPS));  // slice 0 landed (this wave)
   __syncthreads();
   lload(0, 0);
@@ -602,7 +670,7 @@ __global__ __launch_bounds__(256) void gemm_dl_kernel(GemmArgs p) {
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may still be landing in LDS
   __syncthreads();
-  gemm_epilogue<bf16, BM, BN, EPI>(p, acc, reinterpret_cast<float *>(lds), m0, n0, bias_g, g);
+  epi.store(acc, reinterpret_cast<float *>(lds));
 }
 
 template <typename T, int BM, int BN, int NWN = 2, int NW = 4>
