@@ -13,14 +13,15 @@ from tests.gpu_helpers import announce, dev_tensor, rel_l2, require_gpu, storage
 pytestmark = pytest.mark.gpu
 
 
-def _gemm_case(dtype, epi, M, N, K, tile, seed=0):
+def _gemm_case(dtype, epi, M, N, K, tile, seed=0, with_bias=True, with_gate=True):
     rng = np.random.default_rng(seed)
     A = storage_round(rng.standard_normal((M, K)), dtype)
     W = storage_round(rng.standard_normal((N, K)) * 0.05, dtype)
-    b = storage_round(rng.standard_normal(N) * 0.1, dtype)
-    gate = rng.standard_normal(N).astype(np.float32)
+    b = storage_round(rng.standard_normal(N) * 0.1, dtype) if with_bias else np.zeros(N)
+    gate = rng.standard_normal(N).astype(np.float32) if with_gate else np.ones(N, np.float32)
     x0 = rng.standard_normal((M, N)).astype(np.float32)
-    Ad, Wd, bd = dev_tensor(A, dtype), dev_tensor(W, dtype), dev_tensor(b, dtype)
+    Ad, Wd = dev_tensor(A, dtype), dev_tensor(W, dtype)
+    bd = dev_tensor(b, dtype) if with_bias else None
     if epi in (B.DIT_EPI_STORE, B.DIT_EPI_GELU):
         out = torch.zeros((M, N), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
                           device="cuda")
@@ -28,7 +29,7 @@ def _gemm_case(dtype, epi, M, N, K, tile, seed=0):
         out = torch.from_numpy(x0).cuda()
     else:
         out = torch.zeros((M, N), dtype=torch.float32, device="cuda")
-    gd = torch.from_numpy(gate).cuda() if epi == B.DIT_EPI_RESIDUAL else None
+    gd = torch.from_numpy(gate).cuda() if epi == B.DIT_EPI_RESIDUAL and with_gate else None
     gemm(dtype, epi, Ad, Wd, bd, out, gate=gd, tile=tile)
     torch.cuda.synchronize()
     C = oracle.linear(A, W, b)
@@ -69,6 +70,20 @@ def test_gemm_bf16_three_stage_ring(epi, M, N, K):
     assert err < tol, err
 
 
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
+                                 B.DIT_EPI_STORE_F32])
+def test_gemm_bf16_without_bias_or_gate(tile, epi):
+    # no bias (and, for the residual epilogue, no gate): the epilogue reads the
+    # missing operand as zero (one), on a ragged shape where the last column
+    # runs take the scalar path
+    require_gpu()
+    announce("gemm bf16 no bias/gate", tile, epi)
+    err = _gemm_case("bf16", epi, 300, 260, 136, tile, seed=5, with_bias=False, with_gate=False)
+    tol = 5e-3 if epi in (B.DIT_EPI_STORE, B.DIT_EPI_GELU) else 1e-5
+    assert err < tol, err
+
+
 @pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
                                  B.DIT_EPI_STORE_F32])
 @pytest.mark.parametrize("M,N,K", [(16, 64, 16), (100, 72, 264), (77, 16, 64)])
@@ -97,3 +112,10 @@ def test_gemm_full_size_sampled_rows():
     ref = oracle.gelu_tanh(oracle.linear(Ah, to_np(W), to_np(b)))
     got = to_np(out[torch.from_numpy(rows).cuda()])
     assert rel_l2(got, ref) < 5e-3
+
+
+@pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_RESIDUAL])
+def test_gemm_f32_without_bias_or_gate(epi):
+    require_gpu()
+    announce("gemm f32 no bias/gate", epi)
+    assert _gemm_case("f32", epi, 100, 72, 264, 0, seed=6, with_bias=False, with_gate=False) < 1e-5
