@@ -51,6 +51,19 @@ __device__ __forceinline__ void mma32(const f32x8 &a, const f32x8 &b, f32x16 &c)
 // 16-byte global/LDS vector moves.
 struct alignas(16) U128 { uint32_t w[4]; };
 
+// Raw buffer resource over `bytes` bytes: loads at offsets past the end
+// return zero, so ragged edges and absent operands (an empty range) need no
+// branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(U128, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+constexpr uint32_t OOB = 0x80000000u;  // an offset past every operand (sizes < 2^31 bytes)
+
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediate for "at most n vector-memory operations outstanding"

@@ -40,18 +40,6 @@ __device__ __forceinline__ typename Frag<T>::type lds_frag(const T *p) {
   }
 }
 
-// Raw buffer resource over `bytes` bytes: loads at offsets past the end
-// return zero, which handles ragged M, N and K without branches.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ U128 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(U128, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-constexpr uint32_t OOB = 0x80000000u;  // an offset past every operand (sizes < 2^31 bytes)
-
 // Order this wave's LDS writes before its later LDS reads (other lanes' data).
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");

@@ -26,7 +26,19 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x
   if (row >= rows) return;
   const float *xr = x + (int64_t)row * D;
   const int nv = D >> 2;  // float4 count
-  f32x4 v[NV];
+  f32x4 v[NV], sh[NV], sc[NV];
+  // the modulation vectors go out with the row: read after the reductions,
+  // each group's load would be another memory round trip before its store
+  if (shift) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = lane + i * 64;
+      if (c < nv) {
+        sh[i] = *reinterpret_cast<const f32x4 *>(shift + 4 * c);
+        sc[i] = *reinterpret_cast<const f32x4 *>(scale + 4 * c);
+      }
+    }
+  }
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -58,10 +70,8 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = (v[i][e] - mu) * rstd;
       if (shift) {
-        const f32x4 sh = *reinterpret_cast<const f32x4 *>(shift + 4 * c);
-        const f32x4 sc = *reinterpret_cast<const f32x4 *>(scale + 4 * c);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = o[e] * (1.0f + sc[e]) + sh[e];
+        for (int e = 0; e < 4; ++e) o[e] = o[e] * (1.0f + sc[i][e]) + sh[i][e];
       }
       if constexpr (sizeof(T) == 2) {
         bf16x4 b;
@@ -259,7 +269,34 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T *__restrict__ W, cons
                                                    int silu_in, const void *const *__restrict__ fan,
                                                    int nfan, float *__restrict__ fan_out) {
   constexpr int VEC = 16 / sizeof(T);
+  constexpr int PRE = 4;  // weight pieces per lane read before the input is staged
   __shared__ float xs[GEMV_MAXK];
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool live = n < N;
+  // Everything that does not depend on the input goes out first (the fan-out
+  // row's pointer, the first PRE pieces of the weight row, the bias, the
+  // fan-out value), so that its memory latency overlaps the staging instead
+  // of following it.  Buffer loads (zero past the range, no branch) and a
+  // load through a selected pointer keep the compiler from waiting for them
+  // where they are issued.
+  const T *fp = W;  // fan-out row f = lane (rows past 64 are read at the end)
+  if (live && lane < nfan) fp = static_cast<const T *>(fan[lane]) + n;
+  const T *wr = W + (int64_t)(live ? n : 0) * K;
+  const auto wrs = make_rsrc(W, (uint32_t)((int64_t)N * K * sizeof(T)));
+  const uint32_t wrow = (uint32_t)((int64_t)n * K * sizeof(T));
+  U128 pre[PRE];
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    const int k0 = (lane + i * 64) * VEC;
+    pre[i] = buf_load16(wrs, live && k0 < K ? wrow + (uint32_t)(k0 * sizeof(T)) : OOB);
+  }
+  const auto brs = make_rsrc(b ? static_cast<const void *>(b) : static_cast<const void *>(W),
+                             b ? (uint32_t)(N * sizeof(T)) : 0u);
+  const uint32_t bbits =
+      sizeof(T) == 2 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(brs, n * 2, 0, 0) << 16
+                     : (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(brs, n * 4, 0, 0);
+  const T fv = *fp;
   if (x) {
     for (int k = threadIdx.x; k < K; k += 256) xs[k] = silu_in ? silu(x[k]) : x[k];
   } else {
@@ -271,27 +308,36 @@ __global__ __launch_bounds__(256) void gemv_kernel(const T *__restrict__ W, cons
     }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= N) return;
-  const T *wr = W + (int64_t)n * K;
+  if (!live) return;
   float acc = 0.0f;
-  for (int k0 = lane * VEC; k0 < K; k0 += 64 * VEC) {
+#pragma unroll
+  for (int i = 0; i < PRE; ++i) {
+    const int k0 = (lane + i * 64) * VEC;
+    if (k0 < K) {
+      const T *w = reinterpret_cast<const T *>(&pre[i]);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc += to_f32(w[e]) * xs[k0 + e];
+    }
+  }
+  for (int k0 = (lane + PRE * 64) * VEC; k0 < K; k0 += 64 * VEC) {
     U128 raw = *reinterpret_cast<const U128 *>(wr + k0);
     const T *w = reinterpret_cast<const T *>(&raw);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc += to_f32(w[e]) * xs[k0 + e];
   }
-  const float yv = wave_sum(acc) + (b ? to_f32(b[n]) : 0.0f);  // in every lane
+  const float yv = wave_sum(acc) + __uint_as_float(bbits);  // in every lane
   if (lane == 0) y[n] = yv;
   for (int f = lane; f < nfan; f += 64)
-    fan_out[(int64_t)f * N + n] = yv + to_f32(static_cast<const T *>(fan[f])[n]);
+    fan_out[(int64_t)f * N + n] =
+        yv + to_f32(f == lane ? fv : static_cast<const T *>(fan[f])[n]);
 }
 
 hipError_t launch_gemv(DType dt, const void *W, const void *b, const float *x, float t, float *y,
                        int N, int K, bool silu_in, const void *const *fan, int nfan, float *fan_out,
                        hipStream_t s) {
   if (K > GEMV_MAXK || (!x && (K & 1)) || (nfan > 0 && (!fan || !fan_out))) return hipErrorInvalidValue;
+  // 32-bit buffer offsets over the weight matrix
+  if ((int64_t)N * K * (dt == DT_BF16 ? 2 : 4) >= (int64_t)OOB) return hipErrorInvalidValue;
   dim3 grid((N + 3) / 4);
   if (dt == DT_BF16)
     dit_launch(gemv_kernel<bf16>, grid, 256, s, static_cast<const bf16 *>(W), static_cast<const bf16 *>(b),
