@@ -103,6 +103,8 @@ def _attention_case(cfg, sq, sk, v_const=None, rng=RNG):
     ("tiny_f32", 16, 16), ("tiny_f32", 16, 8), ("tiny_f32", 130, 77),
     ("image_s_bf16", 1024, 1024), ("image_s_bf16", 1024, 256), ("image_s_bf16", 300, 1000),
     ("image_s_bf16", 1, 1), ("image_s_bf16", 129, 65),
+    # small grids split the keys in two ranges: even tile counts, ragged last tile
+    ("image_s_bf16", 200, 250), ("image_s_bf16", 100, 2000),
     ("wan1p3b_bf16", 777, 1500), ("wan1p3b_bf16", 256, 512), ("wan1p3b_bf16", 64, 3),
     # >= 256 workgroups of 256 queries: the two-query-block kernel (head_dim 128)
     ("wan14b_bf16", 1700, 1000), ("wan14b_bf16", 1537, 64), ("image_l_bf16", 2400, 777),
@@ -118,12 +120,15 @@ def test_attention_parity(name, sq, sk):
     assert rel_l2(o, ref.reshape(sq, -1)) < tol
 
 
-@pytest.mark.parametrize("name", ["image_s_bf16", "wan1p3b_bf16"])
-def test_attention_constant_values(name):
+@pytest.mark.parametrize("name,sk", [("image_s_bf16", 333), ("image_s_bf16", 1000),
+                                     ("wan1p3b_bf16", 333)])
+def test_attention_constant_values(name, sk):
+    # V = 1: every output is exactly a normalised sum of ones, whatever the
+    # split of the keys (an odd tile count at 333 keys, an even one at 1000)
     require_gpu()
     cfg = workload(name)
-    announce("attention V=1", name)
-    o, *_ = _attention_case(cfg, 200, 333, v_const=1.0)
+    announce("attention V=1", name, sk)
+    o, *_ = _attention_case(cfg, 200, sk, v_const=1.0)
     assert np.max(np.abs(o - 1.0)) <= 2 ** -7
 
 
