@@ -698,20 +698,16 @@ bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) 
 
 // Tile choice (measured on MI355X): 256x256 with 8 waves (two per SIMD, 3-15%
 // faster than 4 waves on every large step shape) once the grid has at least
-// half a tile per CU; else 64x64 while those tiles fit one wave of
-// workgroups (MLP-1 at 1024 tokens, 768 tiles: 11.0 against 12.0 us for
-// 128x128); else 128x128 from half a tile per CU for the plain epilogues but
-// from one per CU for the split store with RoPE, whose heavier epilogue
-// favours more, smaller tiles; else 64x64.
-static int pick_tile(int M, int N, int groups, Epilogue epi) {
+// half a tile per CU; else 64x64.  Below that size 64x64 beat 128x128
+// everywhere it was timed: MLP-1 at 1024 tokens (768 tiles, 11.0 against
+// 12.0 us), and, once the 64x64 epilogue read its operands ahead, the grouped
+// cross K/V projection at 1024 tokens (1152 tiles) and the guided step's QKV
+// and MLP-1 at 2048 rows (1152 and 1536 tiles): the guided 1024-token step
+// went from 1.818 to 1.738 ms.  128x128 remains for explicit requests.
+static int pick_tile(int M, int N, int groups) {
   const int64_t G = groups > 1 ? groups : 1;
   const int64_t t256 = G * ((M + 255) / 256) * ((N + 255) / 256);
-  const int64_t t128 = G * ((M + 127) / 128) * ((N + 127) / 128);
-  const int64_t t64 = G * ((M + 63) / 64) * ((N + 63) / 64);
-  if (t256 >= 128) return 4;
-  if (t64 <= 768) return 3;  // one wave of 64x64 workgroups (two or three per CU)
-  if (t128 >= (epi == EPI_SPLIT ? 256 : 128)) return 2;
-  return 3;
+  return t256 >= 128 ? 4 : 3;
 }
 
 hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile) {
@@ -720,7 +716,7 @@ hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s,
   if (a.gw ? (!a.gbias || a.groups < 1) : (a.W == nullptr || a.groups > 1)) return hipErrorInvalidValue;
   if (!gemm_offsets_fit(dt, a.M, a.lda, a.N, a.ldw)) return hipErrorInvalidValue;
   if (dt == DT_BF16) {
-    if (tile == 0) tile = pick_tile(a.M, a.N, a.groups, epi);
+    if (tile == 0) tile = pick_tile(a.M, a.N, a.groups);
     // a split store needs every wave's column strip inside one segment: 128
     // columns for tile 1, 64 for tiles 2 and 4, 32 for tile 3
     if (epi == EPI_SPLIT && tile == 1 && a.seg_width % 128 != 0) tile = 4;
