@@ -60,6 +60,22 @@ def test_gemm_bf16_tiles(tile, epi, M, N, K):
 
 @pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
                                  B.DIT_EPI_STORE_F32])
+@pytest.mark.parametrize("M,N,K", [
+    (300, 260, 64),      # 64x64, five-stage ring
+    (1000, 2300, 136),   # 64x64, 576 tiles: three-stage ring
+    (2048, 3072, 200),   # 64x64, 1536 tiles (the size that used to take 128x128)
+    (4096, 3584, 256),   # 224 tiles of 256x256
+])
+def test_gemm_bf16_automatic_tile(epi, M, N, K):
+    require_gpu()
+    announce("gemm bf16 automatic tile", epi, M, N, K)
+    err = _gemm_case("bf16", epi, M, N, K, 0, seed=7)
+    tol = 5e-3 if epi in (B.DIT_EPI_STORE, B.DIT_EPI_GELU) else 1e-5
+    assert err < tol, err
+
+
+@pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
+                                 B.DIT_EPI_STORE_F32])
 @pytest.mark.parametrize("M,N,K", [(1000, 2300, 520), (1000, 2300, 64)])
 def test_gemm_bf16_three_stage_ring(epi, M, N, K):
     # 64x64 tiles on a grid of 513 .. 768 tiles take the three-stage ring
