@@ -82,6 +82,24 @@ def test_layernorm_modulate(name):
     assert rel_l2(to_np(y_plain), oracle.layer_norm(x, cfg.ln_eps)) < tol
 
 
+@pytest.mark.parametrize("D", [1000, 1536, 3584])
+def test_layernorm_modulate_widths(D):
+    # the other row widths of the workloads (1536, 3584) and one whose last
+    # 16-byte group per lane is partial (1000 = 250 groups of 4), so the
+    # masked reads of x, shift and scale all run
+    require_gpu()
+    announce("layernorm_modulate width", D)
+    rows, eps = 45, 1e-6
+    x = (RNG.standard_normal((rows, D)) * 2 - 0.5).astype(np.float32)
+    sh = RNG.standard_normal(D).astype(np.float32)
+    sc = RNG.standard_normal(D).astype(np.float32)
+    y = torch.empty((rows, D), dtype=torch.bfloat16, device="cuda")
+    layernorm_modulate("bf16", eps, torch.from_numpy(x).cuda(), torch.from_numpy(sh).cuda(),
+                       torch.from_numpy(sc).cuda(), y)
+    torch.cuda.synchronize()
+    assert rel_l2(to_np(y), oracle.modulate(oracle.layer_norm(x, eps), sh, sc)) < 5e-3
+
+
 # ----------------------------------------------------------------- attention
 def _attention_case(cfg, sq, sk, v_const=None, rng=RNG):
     H, d, D = cfg.heads, cfg.head_dim, cfg.hidden
