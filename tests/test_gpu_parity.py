@@ -40,11 +40,18 @@ def test_euler_constant_velocity_chain():
 
 
 # ----------------------------------------------------------------- time path
-@pytest.mark.parametrize("name", ["tiny_f32", "image_s_bf16", "wan1p3b_bf16"])
-def test_time_embedding(name):
+@pytest.mark.parametrize("name,over", [
+    ("tiny_f32", {}), ("image_s_bf16", {}), ("wan1p3b_bf16", {}),
+    # more than 64 blocks: modulation rows past the first 64 per wave
+    ("tiny_f32", dict(num_blocks=70)),
+    # width 2560 in bf16: weight pieces past the ones read before the input
+    ("image_s_bf16", dict(hidden=2560, heads=20, head_dim=128, rope=(0, 64, 64),
+                          mlp_hidden=512, text_dim=2560)),
+])
+def test_time_embedding(name, over):
     require_gpu()
-    cfg = workload(name, num_blocks=2, latent=(1, 8, 8))
-    announce("time_embedding", name)
+    cfg = workload(name, **{"num_blocks": 2, "latent": (1, 8, 8), **over})
+    announce("time_embedding", name, over)
     prm = SP.make_params(cfg)
     m = DeviceDiT(cfg, prm)
     for t in (1000.0, 617.25, 0.0):
