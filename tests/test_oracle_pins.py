@@ -425,3 +425,215 @@ def test_cfg_affine_in_the_scale():
     np.testing.assert_allclose(Vs[2.0] - Vs[1.0], Vp - Vn, atol=1e-13)
     X4, V4 = oracle.denoise_step_cfg(X0, E, En, 250.0, 0.25, 0.2, 4.0, params, cfg)
     np.testing.assert_allclose(X4, X0 + (0.2 - 0.25) * V4, atol=1e-15)
+
+
+# ----------------------------------------------------------------- closed forms through
+# the time path, the final layer, the pre-cross-attention LayerNorm, the cross keys,
+# the self-attention modulation and the rotary on keys.  Each builds selection or
+# identity weights so the expected value is a scalar formula evaluated here with
+# ``math``, not by calling the oracle piece under test.
+def _silu(z):
+    return z / (1.0 + math.exp(-z))
+
+
+def _alt(n):
+    """The +1, -1, +1, ... pattern: mean 0 over an even width, so LayerNorm of
+    alpha * alt + beta is alt * alpha / sqrt(alpha^2 + eps) exactly."""
+    return np.array([1.0 if e % 2 == 0 else -1.0 for e in range(n)])
+
+
+def _time_weights(D, Z, gate_rows_zero=False):
+    """Selection weights for the time path at t = 0, where the sinusoid is
+    ones on its cosine half and zeros on its sine half."""
+    half = Z // 2
+    t1_w = np.zeros((D, Z))
+    for i in range(D):
+        t1_w[i, i] = -2.0              # cosine half: contributes -2 at t = 0
+        t1_w[i, half + i] = 7.0        # sine half: contributes nothing at t = 0
+    t1_b = np.linspace(-1.0, 0.5, D)
+    t2_w = 3.0 * np.eye(D)
+    t2_b = np.full(D, 0.1)
+    mod_w = np.vstack([(k + 1) * np.eye(D) for k in range(6)])
+    mod_b = np.concatenate([np.full(D, 0.05 * k) for k in range(6)])
+    if gate_rows_zero:
+        for k in (2, 5):
+            mod_w[k * D:(k + 1) * D] = 0
+            mod_b[k * D:(k + 1) * D] = 0
+    g = {"t1_w": t1_w, "t1_b": t1_b, "t2_w": t2_w, "t2_b": t2_b, "mod_w": mod_w, "mod_b": mod_b}
+    temb = np.array([3.0 * _silu(-2.0 + t1_b[i]) + 0.1 for i in range(D)])
+    e = np.array([[(k + 1) * _silu(temb[i]) + 0.05 * k for i in range(D)] for k in range(6)])
+    if gate_rows_zero:
+        e[2] = 0
+        e[5] = 0
+    return g, temb, e
+
+
+def test_time_embedding_closed_form():
+    # Catches: SiLU dropped between the two time layers or before the shared
+    # modulation projection; bias added after the activation; the sine half
+    # first; the six modulation vectors reshaped in the wrong order.
+    D, Z = 6, 16
+    g, temb, e = _time_weights(D, Z)
+    t_o, e_o = oracle.time_embedding(0.0, g, Z)
+    np.testing.assert_allclose(t_o, temb, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(e_o, e, rtol=0, atol=1e-15)
+
+
+def test_context_projection_selection():
+    # A selection text projection (text width 12 -> hidden 8) copies the
+    # chosen columns and adds the bias; equal widths leave the context alone.
+    cfg = tiny_cfg(text_dim=12)
+    sel = np.array([11, 0, 5, 3, 9, 1, 7, 2])
+    w = np.zeros((8, 12))
+    w[np.arange(8), sel] = 1.0
+    b = np.arange(8) * 0.25
+    E = RNG.normal(0, 1, (5, 12))
+    c = oracle.context_projection(E, {"txt_w": w, "txt_b": b}, cfg)
+    np.testing.assert_array_equal(c, E[:, sel] + b)
+    same = tiny_cfg()
+    E8 = RNG.normal(0, 1, (5, 8))
+    np.testing.assert_array_equal(oracle.context_projection(E8, {"txt_w": None}, same), E8)
+
+
+def _structured_latents(cfg, alpha, beta):
+    """Latents whose every patch vector is alpha_n * alt + beta_n (patch
+    (1, 2, 2): patch element e = 4c + 2j + k, and alt flips with k)."""
+    C = cfg.in_channels
+    F, H, W = cfg.latent
+    G = (F, H // 2, W // 2)
+    X = np.zeros((C, F, H, W))
+    for c in range(C):
+        for f in range(F):
+            for h in range(H):
+                for w in range(W):
+                    n = (f * G[1] + h // 2) * G[2] + w // 2
+                    X[c, f, h, w] = alpha[n] * (1.0 if w % 2 == 0 else -1.0) + beta[n]
+    return X
+
+
+def test_forward_closed_form_text_projection_cross_value_and_final_layer():
+    # One block with both gates zero, so only its ungated cross-attention
+    # branch changes the residual.  One context token: the softmax weight is 1
+    # and that branch adds W_co (W_cv c0 + b_cv) + b_co = c0 to every token
+    # (identity value and output weights).  c0 comes from a selection text
+    # projection with a bias, arranged so that c0 = gam * alt + kap.  Patch
+    # embedding is the identity, so every token stays of the form
+    # a * alt + b and each LayerNorm is a closed form.  The final layer's
+    # shift and scale are the head table plus temb from the closed-form time
+    # path.  Catches: the text projection skipped or its bias dropped; the
+    # final layer's shift and scale swapped, its LayerNorm dropped, the head
+    # table or temb ignored; SiLU dropped anywhere in the time path.
+    cfg = tiny_cfg(text_dim=12, freq_dim=16)
+    D, eps = cfg.hidden, cfg.ln_eps
+    alt = _alt(D)
+    g, temb, e = _time_weights(D, cfg.freq_dim, gate_rows_zero=True)
+    sel = np.array([2, 7, 0, 11, 4, 9, 1, 5])
+    txt_w = np.zeros((D, 12))
+    txt_w[np.arange(D), sel] = 1.0
+    gam1, kap1, gam2, kap2 = 0.4, -0.3, 0.25, 0.6
+    E = RNG.normal(0, 1, (1, 12))
+    E[0, sel] = gam1 * alt + kap1
+    T = np.stack([np.linspace(-0.5, 0.5, D), np.linspace(0.3, -0.2, D)])
+    out_b = RNG.normal(0, 0.5, D)
+    g.update({"txt_w": txt_w, "txt_b": gam2 * alt + kap2, "pe_w": np.eye(D), "pe_b": np.zeros(D),
+              "head_table": T, "out_w": np.eye(D), "out_b": out_b})
+    blk = rand_block(cfg)
+    blk["table"][:] = 0
+    blk["ckv_w"] = np.vstack([RNG.normal(0, 1, (D, D)), np.eye(D)])
+    blk["ckv_b"] = np.concatenate([RNG.normal(0, 1, D), np.zeros(D)])
+    blk["co_w"] = np.eye(D)
+    blk["co_b"] = np.zeros(D)
+    params = {"global": g, "blocks": [blk]}
+    S = 8
+    alpha = np.array([0.5, 1.5, -0.7, 2.0, 0.9, -1.2, 0.3, 1.1])
+    beta = np.array([0.2, -1.0, 3.0, 0.0, -0.4, 1.7, 0.8, -2.2])
+    X = _structured_latents(cfg, alpha, beta)
+    V = oracle.dit_forward(X, E, 0.0, params, cfg)
+    gam = gam1 + gam2
+    expect = np.zeros_like(X)
+    C = cfg.in_channels
+    for c in range(C):
+        for f in range(cfg.latent[0]):
+            for h in range(cfg.latent[1]):
+                for w in range(cfg.latent[2]):
+                    n = (f * 2 + h // 2) * 2 + w // 2
+                    el = 4 * c + 2 * (h % 2) + (w % 2)
+                    a = alpha[n] + gam
+                    r = a / math.sqrt(a * a + eps)
+                    expect[c, f, h, w] = (r * alt[el] * (1.0 + T[1, el] + temb[el])
+                                          + T[0, el] + temb[el] + out_b[el])
+    assert S == 8
+    np.testing.assert_allclose(V, expect, rtol=0, atol=1e-12)
+
+
+def test_block_two_key_cross_attention_closed_form():
+    # Gates zero, so the block adds only its cross branch.  Tokens are
+    # alpha_n * alt + beta_n, so the LayerNorm in front of the cross query is
+    # r_n * alt.  With identity query, key, value and output weights and the two
+    # context rows +a * alt and -a * alt, each head's scores are +-2 r_n a
+    # (head width 4, scaled by 1/2), the first key's weight is sigma(4 r_n a),
+    # and the block adds tanh(2 r_n a) * a * alt.  Catches: the LayerNorm before
+    # cross-attention dropped (the scores would follow alpha_n, not r_n); keys
+    # or values built from one context row; the softmax scale missing.
+    cfg = tiny_cfg()
+    D, eps, a = cfg.hidden, cfg.ln_eps, 0.25
+    alt = _alt(D)
+    p = rand_block(cfg)
+    p["cq_w"], p["cq_b"] = np.eye(D), np.zeros(D)
+    p["ckv_w"], p["ckv_b"] = np.vstack([np.eye(D), np.eye(D)]), np.zeros(2 * D)
+    p["co_w"], p["co_b"] = np.eye(D), np.zeros(D)
+    alpha = np.array([0.3, 2.5, -1.5, 0.8, 4.0, -0.2, 1.3, -3.0])
+    beta = RNG.normal(0, 2, 8)
+    x = alpha[:, None] * alt + beta[:, None]
+    c = np.stack([a * alt, -a * alt])
+    mod = RNG.normal(0, 1, (6, D))
+    mod[2] = 0
+    mod[5] = 0
+    pos = oracle.token_positions((1, 2, 4))
+    out = oracle.dit_block(x, c, mod, p, cfg, pos)
+    expect = np.array([x[n] + math.tanh(2 * (alpha[n] / math.sqrt(alpha[n] ** 2 + eps)) * a)
+                       * a * alt for n in range(8)])
+    np.testing.assert_allclose(out, expect, rtol=0, atol=1e-13)
+
+
+def test_block_self_attention_modulation_order():
+    # scale_a = -1 turns the modulated self-attention input into shift_a for
+    # every token, so all values are W_v shift_a + b_v and every attention row
+    # returns that vector whatever the queries, keys and RoPE are.  The block
+    # then adds gate_a * (W_o (W_v shift_a + b_v) + b_o).  Catches: shift and
+    # scale of the self-attention modulation swapped (the input would then
+    # follow each token's LayerNorm), or modulation by (scale) instead of
+    # (1 + scale).
+    cfg = tiny_cfg()
+    D = cfg.hidden
+    p = rand_block(cfg)
+    p["co_w"][:] = 0
+    p["co_b"][:] = 0
+    x, c, pos = _block_inputs(cfg)
+    mod = RNG.normal(0, 1, (6, D))
+    mod[1] = -1.0
+    mod[5] = 0
+    v = p["qkv_w"][2 * D:] @ mod[0] + p["qkv_b"][2 * D:]
+    expect = x + mod[2] * (p["o_w"] @ v + p["o_b"])
+    np.testing.assert_allclose(oracle.dit_block(x, c, mod, p, cfg, pos), expect, atol=1e-13)
+
+
+def test_block_rotary_relative_positions():
+    # Rotary on both queries and keys makes self-attention scores depend only
+    # on position differences, so a common shift of every token's grid position
+    # leaves the block output unchanged, while moving tokens relative to each
+    # other changes it.  Catches: rotary applied to the queries only or to the
+    # keys only, or to neither.
+    cfg = tiny_cfg(head_dim=8, heads=1, rope=(2, 2, 4))
+    D = cfg.hidden
+    p = rand_block(cfg, std=0.8)
+    x, c, _ = _block_inputs(cfg)
+    pos = oracle.token_positions((2, 2, 2))
+    mod = RNG.normal(0, 0.5, (6, D))
+    mod[2] = 1.0
+    base = oracle.dit_block(x, c, mod, p, cfg, pos)
+    shifted = oracle.dit_block(x, c, mod, p, cfg, pos + np.array([3, 5, 11]))
+    np.testing.assert_allclose(shifted, base, rtol=0, atol=1e-12)
+    moved = pos.copy()
+    moved[:, 2] *= 3
+    assert np.max(np.abs(oracle.dit_block(x, c, mod, p, cfg, moved) - base)) > 1e-4
