@@ -10,6 +10,7 @@
 // "Model Configuration Conventions", section "Sampling And Geometry").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <new>
@@ -132,6 +133,14 @@ bool plan_layout(const dit_config &c, Plan &p) {
   return true;
 }
 
+// The attention kernel addresses keys and transposed values through buffer
+// resources with 32-bit byte offsets and ranges: every key row of the last
+// (partial) 64-key tile and the whole value matrix must lie below 2^31 bytes.
+bool attention_offsets_fit(int64_t es, int64_t D, int64_t sk, int64_t ldk, int64_t ldv) {
+  const int64_t lim = (int64_t)1 << 31;
+  return ((sk + 63) / 64 * 64 + 64) * ldk * es < lim && D * ldv * es < lim;
+}
+
 dit_status check_config(const dit_config *c) {
   if (!c) return DIT_ERR_INVALID_ARG;
   if (c->dtype != DIT_F32 && c->dtype != DIT_BF16) return DIT_ERR_INVALID_ARG;
@@ -152,7 +161,8 @@ dit_status check_config(const dit_config *c) {
   const int64_t P = (int64_t)c->in_channels * c->patch_f * c->patch_h * c->patch_w;
   if (c->hidden % 8 || c->mlp_hidden % 8 || c->text_dim % 8 || c->freq_dim % 8 || P % 8)
     return DIT_ERR_UNSUPPORTED;
-  if (c->hidden > 5120 || c->hidden > 8192 || c->freq_dim > 8192) return DIT_ERR_UNSUPPORTED;
+  // the LayerNorm keeps a row in registers (at most 5120 wide)
+  if (c->hidden > 5120 || c->freq_dim > 8192) return DIT_ERR_UNSUPPORTED;
   const int64_t S = (int64_t)(c->lat_f / c->patch_f) * (c->lat_h / c->patch_h) *
                     (c->lat_w / c->patch_w);
   if (S > (int64_t)1 << 30) return DIT_ERR_UNSUPPORTED;
@@ -164,8 +174,21 @@ dit_status check_config(const dit_config *c) {
   if (c->guidance && S % 8) return DIT_ERR_UNSUPPORTED;
   const int64_t rows = c->guidance ? 2 * S : S;
   const DType dt = c->dtype == DIT_BF16 ? DT_BF16 : DT_F32;
-  if (!gemm_offsets_fit(dt, rows, c->mlp_hidden, 3 * (int64_t)c->hidden, c->mlp_hidden) ||
-      !gemm_offsets_fit(dt, c->ctx_len_max, c->text_dim, c->mlp_hidden, c->hidden))
+  // every projection of the step: activations [rows, D | F | P] and weights
+  // with up to max(3D, F) rows of width D or F; the context projection's
+  // [L, text_dim] and [D, text_dim]
+  const int64_t wide = std::max<int64_t>(std::max<int64_t>(c->hidden, c->mlp_hidden), P);
+  const int64_t wrows = std::max<int64_t>(3 * (int64_t)c->hidden, c->mlp_hidden);
+  if (!gemm_offsets_fit(dt, rows, wide, wrows, std::max(c->hidden, c->mlp_hidden)) ||
+      !gemm_offsets_fit(dt, c->ctx_len_max, std::max(c->text_dim, c->hidden),
+                        std::max(c->hidden, c->mlp_hidden), c->text_dim))
+    return DIT_ERR_UNSUPPORTED;
+  // self-attention keys [S, D] and values [D, S_pad per sequence]; cross keys
+  // [L, D] and values [D, L_pad per context]
+  const int64_t es = dt == DT_BF16 ? 2 : 4, seqs = c->guidance ? 2 : 1;
+  if (!attention_offsets_fit(es, c->hidden, S, c->hidden, seqs * (int64_t)round_up((size_t)S, 64)) ||
+      !attention_offsets_fit(es, c->hidden, c->ctx_len_max, c->hidden,
+                             seqs * (int64_t)round_up((size_t)c->ctx_len_max, 64)))
     return DIT_ERR_UNSUPPORTED;
   return DIT_OK;
 }
@@ -871,6 +894,7 @@ dit_status dit_attention(int32_t dtype, int32_t heads, int32_t head_dim, const v
   const int64_t D = (int64_t)heads * head_dim;
   if (ldq < D || ldk < D || ldo < D || ldv < (int64_t)round_up((size_t)sk, 64)) return DIT_ERR_SHAPE;
   if ((ldq | ldk | ldv | ldo) & 7) return DIT_ERR_INVALID_ARG;
+  if (!attention_offsets_fit(dtype == DIT_BF16 ? 2 : 4, D, sk, ldk, ldv)) return DIT_ERR_UNSUPPORTED;
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   AttnArgs a{q, ldq, k, ldk, vt, ldv, o, ldo, sq, sk, heads, head_dim, scale_log2};
   return hip_status(launch_attention(dtype == DIT_BF16 ? DT_BF16 : DT_F32, a,

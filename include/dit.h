@@ -153,7 +153,14 @@ dit_status dit_workspace_size(const dit_config *cfg, size_t *bytes);
  * aligned), bind them and the caller's workspace (device, >= the size above,
  * 256-byte aligned) to a new handle, and enqueue on `stream` the
  * precomputation of the rotary cos/sin tables into the workspace.  The handle
- * owns only host memory; release it with dit_destroy. */
+ * owns only host memory; release it with dit_destroy.
+ * The handle stands for the loaded transformer of page "Support New Diffusion
+ * Models - SGLang Documentation": section "Read the Reference First" asks for
+ * the latent shape and packing, the rotary style and the conditioning tensors
+ * that the model fixes once, and section "Verify the Port" lists a rotary
+ * shape or style mismatch among the failure points, which is why the rotary
+ * split and base are fields of the configuration and their tables are built
+ * here, once, rather than per call. */
 dit_status dit_create(const dit_config *cfg, const dit_weights *weights, void *workspace,
                       size_t workspace_bytes, void *stream, dit_model **out);
 
@@ -168,7 +175,16 @@ dit_status dit_destroy(dit_model *model);
  *        step passes shared projection + the block's table; a caller may pass
  *        any values).
  * 0 <= block < num_blocks, 1 <= ctx_len <= ctx_len_max.  Uses the workspace:
- * calls on one handle must not overlap on different streams. */
+ * calls on one handle must not overlap on different streams.
+ * The block is the repeated unit of the denoiser's transformer that page
+ * "Support New Diffusion Models - SGLang Documentation", section "5.
+ * Distributed and memory integration", names as the unit of layerwise offload
+ * and of sequence parallelism; page "Disaggregated Diffusion Pipeline",
+ * section "Quick Start", places the loop over these blocks in the denoiser
+ * role.  Its contents (adaLN-modulated self-attention with rotary, plain
+ * LayerNorm and ungated cross-attention to the context, adaLN-modulated GELU
+ * MLP, gated residuals) are the plainest reading of that block; the pages
+ * print no formula for it. */
 dit_status dit_block_forward(dit_model *model, int32_t block, float *x, const void *ctx,
                              int32_t ctx_len, const float *mod, void *stream);
 
@@ -265,7 +281,14 @@ dit_status dit_denoise_step_cached(dit_model *model, float *X, const void *ctx,
                                    void *stream);
 
 /* Flow Euler update X[i] += (sigma_next - sigma) * v[i] for i < n on device
- * float arrays (layout-agnostic).  n == 0 is a no-op. */
+ * float arrays (layout-agnostic).  n == 0 is a no-op; X and v must be 16-byte
+ * aligned, n >= 0.  Page "Model Configuration Conventions", section "Sampling
+ * And Geometry", names the flow-prediction denoisers and their flow shift;
+ * page "Support New Diffusion Models - SGLang Documentation", section "4.
+ * Last-Resort Before-Denoising Stage", passes the sigma list beside the
+ * timesteps.  A flow-prediction network outputs a velocity, and the first
+ * order step between two noise levels moves the latents by their difference
+ * times that velocity. */
 dit_status dit_euler_step(float *X, const float *v, int64_t n, float sigma, float sigma_next,
                           void *stream);
 

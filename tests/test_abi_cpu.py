@@ -185,3 +185,30 @@ def test_cache_workspace_and_validation():
     assert L.dit_cache_state_get(None, None) == B.DIT_ERR_INVALID_ARG
     assert L.dit_denoise_step_cached(None, 4096, 4096, None, 1, 1.0, 1.0, 0.0, 1.0, None,
                                      None) == B.DIT_ERR_INVALID_ARG
+
+
+def test_attention_rejects_offsets_past_32_bits():
+    # Keys and transposed values are read through 32-bit buffer offsets: a
+    # stride that would put a key row of the last tile, or the value matrix,
+    # at or past 2^31 bytes is refused instead of silently reading zeros.
+    L = B.lib()
+    P = 1 << 20
+    D = 12 * 128
+    ok = L.dit_attention(B.DIT_BF16, 12, 128, P, D, P, 1 << 19, P, 1 << 20, P, D, 4, 1984, None)
+    assert ok == B.DIT_ERR_UNSUPPORTED       # (1984 + 64) * 2^19 * 2 = 2^31 bytes of keys
+    assert L.dit_attention(B.DIT_BF16, 12, 128, P, D, P, D, P, 1 << 20, P, D, 4, 64,
+                           None) == B.DIT_ERR_UNSUPPORTED   # values: 1536 * 2^20 * 2 > 2^31
+    assert L.dit_attention(B.DIT_F32, 12, 128, P, D, P, D, P, 1 << 19, P, D, 4, 64,
+                           None) == B.DIT_ERR_UNSUPPORTED   # fp32: 1536 * 2^19 * 4 > 2^31
+
+
+def test_config_rejects_attention_offsets_past_32_bits():
+    # 2^18 tokens at width 5120 put the activations and keys past 2^31 bytes,
+    # also with a narrow MLP; the configuration is refused before any handle
+    # exists.
+    big = CONFIGS["image_s_bf16"].with_(latent=(1, 1024, 1024), hidden=5120, heads=40,
+                                        head_dim=128, rope=(0, 64, 64), mlp_hidden=8,
+                                        text_dim=5120)
+    with pytest.raises(B.DitError) as e:
+        B.dit_workspace_size(B.make_config(big))
+    assert e.value.status == B.DIT_ERR_UNSUPPORTED
