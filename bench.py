@@ -2,7 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--guidance G] [--offload] [--cache] [--no-cpu-baseline]
-                    [--calibrate-copy]
+                    [--no-other-configs] [--calibrate-copy]
+
+The default workload is the Wan-14B-shaped video DiT (40 blocks, hidden 5120,
+40 heads x 128, MLP 13824, 32760 tokens, text 512 x 4096 projected to 5120),
+the largest of the five workloads and the one that fills one GPU.
 
 A step is one call of dit_denoise_step: time embedding, context projection,
 patch embedding, every DiT block (LayerNorm+adaLN, QKV projection, RoPE,
@@ -31,7 +35,14 @@ Prints ONE JSON line on stdout (diagnostics go to stderr):
                  traffic = HBM bytes per launch from committed rocprofv3
                  FETCH_SIZE / WRITE_SIZE runs (profiles/traffic.json), or null
   attention / gemm   TFLOP/s and fraction of the bf16 MFMA peak, same events
-  cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
+  cpu_baseline   the CPU oracle timed on a bounded sample of the same workload:
+                 whole steps where one fits the budget, else one block, else one
+                 block on a prefix of the token sequence (whole grid rows) at the
+                 full widths; a block sample is converted to steps/s through its
+                 FLOP rate over the step's FLOPs
+  per_config     seconds per step of every other workload, timed after the main
+                 one in the same process (the two smallest: median over five
+                 whole sampling runs)
 """
 from __future__ import annotations
 
@@ -51,7 +62,10 @@ if ROOT not in sys.path:
 METRIC = "denoise steps/sec per config + attention/GEMM TFLOP/s as % bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
-DEFAULT_WORKLOAD = "image_s_bf16"
+# v_exp_f32 issues once per ~8.5 cycles per wave64 per SIMD (measured), i.e.
+# 64 / 8.5 results per clock per SIMD; 4 SIMDs x 256 CUs at 2.4 GHz
+PEAK_EXP_PER_S = 64 / 8.5 * 4 * 256 * 2.4e9
+DEFAULT_WORKLOAD = "wan14b_bf16"
 # Cache-DiT knobs of the pages' GLM-Image denoisers (page "Disaggregated
 # Diffusion Pipeline", section "GLM-Image distributed mode")
 CACHE_KNOBS = dict(fn=2, bn=1, warmup=4, rdt=0.4, max_consecutive=4, taylorseer=True, ts_order=2)
@@ -106,6 +120,13 @@ def kind_work(cfg, nb: int = 1, offload: bool = False) -> dict:
     }
 
 
+def exp_work(cfg, nb: int = 1) -> dict:
+    """Exponentials per launch of the attention kinds: one per (query, key,
+    head) score of the softmax."""
+    S, L, H = cfg.tokens, cfg.ctx_len, cfg.heads
+    return {"attention_self": nb * H * S * S, "attention_cross": nb * H * S * L}
+
+
 def source_hash(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -127,40 +148,111 @@ def measured_traffic(kernel_kind: str, workload: str):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(cfg, prm, X0, E, budget_s: float = 20.0, E_neg=None, g=None) -> dict:
-    """The oracle as it stands, timed on the host cores over the first steps of
-    the same chain (as many as fit the budget, at least one); with E_neg and g,
-    the oracle's guided step."""
-    import oracle
+def block_flops(cfg, S: int) -> int:
+    """Algorithmic FLOPs of one DiT block over S tokens at the workload's widths
+    (projections, the cross K / V of the context, both attentions)."""
+    D, F, L = cfg.hidden, cfg.mlp_hidden, cfg.ctx_len
+    return 12 * S * D * D + 4 * L * D * D + 4 * S * D * F + 4 * S * S * D + 4 * S * L * D
+
+
+def plan_cpu_sample(cfg, budget_s: float, rate_flops: float):
+    """Which oracle unit fits the budget at an assumed host FLOP rate:
+    ("steps", None) when one whole step does, else ("block", S) when one whole
+    block does, else ("block_prefix", n): one block on the first n tokens, n a
+    whole number of grid rows (at least one)."""
+    if cfg.flops_per_step()["total"] / rate_flops <= budget_s:
+        return ("steps", None)
+    S = cfg.tokens
+    if block_flops(cfg, S) / rate_flops <= budget_s:
+        return ("block", S)
+    row = cfg.grid[2]
+    n = row
+    while n + row < S and block_flops(cfg, n + row) / rate_flops <= budget_s:
+        n += row
+    return ("block_prefix", n)
+
+
+def host_matmul_rate() -> float:
+    """float64 matmul FLOP/s of the host (numpy's BLAS), for sizing the sample."""
+    a = np.random.default_rng(0).standard_normal((2048, 2048))
+    a @ a
+    t0 = time.perf_counter()
+    for _ in range(3):
+        a @ a
+    return 3 * 2 * 2048 ** 3 / (time.perf_counter() - t0)
+
+
+def _host_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(cfg, prm, X0, E, budget_s: float = 20.0, E_neg=None, g=None) -> dict:
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the same workload (see plan_cpu_sample); with E_neg and g, the oracle's
+    guided step."""
+    import oracle
+    cores = _host_threads()
+    step_flops = cfg.flops_per_step()["total"] * (2 if E_neg is not None else 1)
+    rate = host_matmul_rate()
+    unit, n = plan_cpu_sample(cfg, budget_s, 0.5 * rate * (2 if E_neg is not None else 1))
     sig = oracle.flow_sigmas(cfg.steps, cfg.shift)
-    X = X0.astype(np.float64)
-    done = 0
+    if unit == "steps":
+        X = X0.astype(np.float64)
+        done = 0
+        t0 = time.perf_counter()
+        while done < cfg.steps:
+            t = float(np.float32(1000.0 * sig[done]))
+            if E_neg is None:
+                X, _ = oracle.denoise_step(X, E, t, sig[done], sig[done + 1], prm, cfg)
+            else:
+                X, _ = oracle.denoise_step_cfg(X, E, E_neg, t, sig[done], sig[done + 1], g, prm,
+                                               cfg)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": done / dt, "unit": "steps/s", "cores": cores, "kind": "oracle",
+                "sample": f"first {done} of the {cfg.steps} "
+                          f"{'guided ' if E_neg is not None else ''}denoise steps of {cfg.name}, "
+                          f"float64 numpy oracle, {dt:.1f} s"}
+    # one block (block 0, its own weights) on the first n tokens of the step's
+    # embedded latents, with the step's first modulation and projected context;
+    # the guided step runs it for both contexts
+    g_ = prm["global"]
+    t = float(np.float32(1000.0 * sig[0]))
+    _, e = oracle.time_embedding(t, g_, cfg.freq_dim)
+    p0 = prm["blocks"][0]
+    mod = oracle.block_modulation(e, p0["table"])
+    x = oracle.linear(oracle.patchify(X0, cfg.patch)[:n], g_["pe_w"], g_["pe_b"])
+    pos = oracle.token_positions(cfg.grid)[:n]
+    ctxs = [E] if E_neg is None else [E, E_neg]
+    cs = [oracle.context_projection(c, g_, cfg) for c in ctxs]
     t0 = time.perf_counter()
-    while done < cfg.steps:
-        t = float(np.float32(1000.0 * sig[done]))
-        if E_neg is None:
-            X, _ = oracle.denoise_step(X, E, t, sig[done], sig[done + 1], prm, cfg)
-        else:
-            X, _ = oracle.denoise_step_cfg(X, E, E_neg, t, sig[done], sig[done + 1], g, prm, cfg)
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
+    for c in cs:
+        oracle.dit_block(x, c, mod, p0, cfg, pos)
     dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {done} of the {cfg.steps} {'guided ' if E_neg is not None else ''}"
-                      f"denoise steps of {cfg.name}, float64 numpy oracle, {dt:.1f} s"}
+    flops = len(cs) * block_flops(cfg, n)
+    what = "all" if n == cfg.tokens else f"the first {n} (whole grid rows)"
+    return {"value": flops / dt / step_flops, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"one DiT block of {cfg.name} (block 0, hidden {cfg.hidden}, "
+                      f"{cfg.heads} heads, MLP {cfg.mlp_hidden}, context {cfg.ctx_len}) on {what} "
+                      f"of its {cfg.tokens} tokens{' for both contexts' if len(cs) > 1 else ''}, "
+                      f"float64 numpy oracle: {flops / 1e12:.3f} TFLOP in {dt:.1f} s = "
+                      f"{flops / dt / 1e9:.1f} GFLOP/s; steps/s = that rate over the "
+                      f"{step_flops / 1e12:.2f} TFLOP of one step",
+            "sample_unit": unit, "sample_tokens": n, "block_seconds": dt,
+            "host_matmul_gflops": round(rate / 1e9, 1)}
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--guidance", type=float, default=None,
                     help="time the guided step (classifier-free guidance) at this scale")
@@ -169,6 +261,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cache", action="store_true",
                     help="block caching across steps with the pages' Cache-DiT knobs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the seconds-per-step lines of the other workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (the known-size kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
@@ -265,6 +359,10 @@ def main(argv=None) -> int:
                          "share": round(tms / sum(v[1] for v in prof.values()), 4),
                          ("tflops" if unit == "flop" else "gbs"):
                              round(rate / (1e12 if unit == "flop" else 1e9), 2)}
+        if name in ATTN_KINDS and avg_s > 0:
+            ex = exp_work(cfg, nb)[name] / avg_s
+            kernels[name]["exp_per_s"] = round(ex / 1e12, 3)   # 10^12 exponentials / s
+            kernels[name]["exp_frac"] = round(ex / PEAK_EXP_PER_S, 4)
         log(f"[bench]   {name:20s} {n:6d} x {avg_s * 1e6:9.2f} us  "
             f"{rate / (1e12 if unit == 'flop' else 1e9):9.2f} {'TFLOP/s' if unit == 'flop' else 'GB/s'}")
 
@@ -275,6 +373,10 @@ def main(argv=None) -> int:
 
     peak = PEAK_TFLOPS[cfg.dtype]
     att_tf, gemm_tf = group_rate(ATTN_KINDS), group_rate(GEMM_KINDS)
+    ew = exp_work(cfg, nb)
+    att_ms = sum(prof[k][1] for k in ATTN_KINDS if k in prof)
+    att_exp = (sum(ew[k] * prof[k][0] for k in ATTN_KINDS if k in prof) / (att_ms / 1e3)
+               if att_ms > 0 else 0.0)
 
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     unit, amount = work[dom]
@@ -328,7 +430,9 @@ def main(argv=None) -> int:
                    **({"cache": dict(CACHE_KNOBS, runs_of=cfg.steps)} if args.cache else {})},
         "step_tflops": round(fl["total"] / (ms_per_step / 1e3) / 1e12, 2),
         "step_frac_of_peak": round(fl["total"] / (ms_per_step / 1e3) / 1e12 / peak, 4),
-        "attention": {"tflops": round(att_tf, 2), "frac_of_peak": round(att_tf / peak, 4)},
+        "attention": {"tflops": round(att_tf, 2), "frac_of_peak": round(att_tf / peak, 4),
+                      "exp_per_s": round(att_exp / 1e12, 3),
+                      "exp_frac_of_peak": round(att_exp / PEAK_EXP_PER_S, 4)},
         "gemm": {"tflops": round(gemm_tf, 2), "frac_of_peak": round(gemm_tf / peak, 4)},
         "roofline": roof,
         "kernels": kernels,
@@ -344,16 +448,106 @@ def main(argv=None) -> int:
                           "host_to_device_gbs": round(streamed / (ms_per_step / 1e3) / 1e9, 2)}
         log(f"[bench] offload: {streamed / 1e9:.3f} GB streamed per step, "
             f"{out['offload']['host_to_device_gbs']} GB/s")
+    plain = not (guided or args.offload or args.cache)
+    if plain and cfg.name in CHAIN_MEDIAN:
+        out["chain_median_ms_per_step"] = round(time_chains(m, X0, Ed, sched, 5), 4)
+    m.close()
+    del m, X, Ed, End
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         out["cpu_baseline"] = (cpu_baseline(cfg, prm, X0, E, E_neg=SP.make_ctx(cfg, seed=3),
                                             g=args.guidance) if guided else
                                cpu_baseline(cfg, prm, X0, E))
+        log(f"[bench] cpu_baseline: {out['cpu_baseline']['sample']}")
     else:
         out["cpu_baseline"] = None
-    m.close()
+    del prm
+    if plain and not args.no_other_configs:
+        per = {cfg.name: {"ms_per_step": out["ms_per_step"], "steps_timed": args.steps,
+                          "step_frac_of_peak": out["step_frac_of_peak"]}}
+        if "chain_median_ms_per_step" in out:
+            per[cfg.name]["chain_median_ms_per_step"] = out["chain_median_ms_per_step"]
+        for name in OTHER_CONFIG_STEPS:
+            if name != cfg.name:
+                per[name] = time_other_config(name)
+        out["per_config"] = per
     print(json.dumps(out), flush=True)
     return 0
+
+
+# the two smallest workloads: median over five whole sampling runs
+CHAIN_MEDIAN = ("tiny_f32", "image_s_bf16")
+# steps timed for each workload's seconds-per-step line (after one warm-up
+# step); the two smallest time whole runs instead
+OTHER_CONFIG_STEPS = {"tiny_f32": None, "image_s_bf16": None, "wan1p3b_bf16": 4,
+                      "image_l_bf16": 10, "wan14b_bf16": 3}
+
+
+def time_chains(m, X0, Ed, sched, runs: int) -> float:
+    """Median over ``runs`` whole sampling runs (every step of the schedule,
+    begun afresh from X0) of the run time divided by its steps, in ms."""
+    import torch
+    stream = torch.cuda.current_stream()
+    X = torch.from_numpy(X0).cuda()
+    per = []
+    for _ in range(runs + 1):          # the first run warms up
+        X.copy_(torch.from_numpy(X0))
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t, s0, s1 in sched:
+            m.denoise_step(X, Ed, t, s0, s1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / len(sched))
+    return float(np.median(per[1:]))
+
+
+def time_other_config(name: str) -> dict:
+    """Seconds per plain denoise step of another workload (fresh inputs and
+    model, freed afterwards)."""
+    import torch
+    from diffusion_transformer_denoising_amd import binding as B
+    from diffusion_transformer_denoising_amd.model import DeviceDiT, torch_dtype
+    from synth import params as SP
+    from synth.configs import get_config
+    cfg = get_config(name)
+    t0 = time.perf_counter()
+    prm = SP.make_params(cfg)
+    X0 = SP.make_latents(cfg)
+    m = DeviceDiT(cfg, prm)
+    del prm
+    Ed = torch.from_numpy(SP.make_ctx(cfg)).cuda().to(torch_dtype(cfg))
+    sig = B.dit_flow_sigmas(cfg.steps, cfg.shift)
+    sched = [(float(np.float32(1000.0 * sig[k])), float(sig[k]), float(sig[k + 1]))
+             for k in range(cfg.steps)]
+    k = OTHER_CONFIG_STEPS[name]
+    if k is None:
+        ms = time_chains(m, X0, Ed, sched, 5)
+        rec = {"ms_per_step": round(ms, 4), "chain_median_ms_per_step": round(ms, 4),
+               "runs": 5, "steps_per_run": cfg.steps}
+    else:
+        X = torch.from_numpy(X0).cuda()
+        stream = torch.cuda.current_stream()
+        m.denoise_step(X, Ed, *sched[0])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(k):
+            m.denoise_step(X, Ed, *sched[(1 + i) % cfg.steps])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / k
+        rec = {"ms_per_step": round(ms, 4), "steps_timed": k}
+    peak = PEAK_TFLOPS[cfg.dtype]
+    rec["step_frac_of_peak"] = round(cfg.flops_per_step()["total"] / (ms / 1e3) / 1e12 / peak, 4)
+    m.close()
+    del m
+    torch.cuda.empty_cache()
+    log(f"[bench] {name}: {rec['ms_per_step']:.4f} ms/step ({time.perf_counter() - t0:.1f} s "
+        f"with inputs)")
+    return rec
 
 
 if __name__ == "__main__":

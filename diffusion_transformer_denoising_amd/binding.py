@@ -86,6 +86,7 @@ _SIGS = {
     "dit_cache_state_get": ([c_vp, ctypes.POINTER(dit_cache_state)], c_i32),
     "dit_denoise_step_cached": ([c_vp, c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_f32, c_f32, c_vp,
                                  c_vp], c_i32),
+    "dit_cache_factor_get": ([c_vp, c_i32, c_vp, c_vp], c_i32),
     "dit_euler_step": ([c_vp, c_vp, c_i64, c_f32, c_f32, c_vp], c_i32),
     "dit_flow_sigmas": ([c_i32, c_f64, ctypes.POINTER(c_f64)], c_i32),
     "dit_attention": ([c_i32, c_i32, c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64,
@@ -216,6 +217,10 @@ def dit_cache_state_get(handle: int) -> dit_cache_state:
     st = dit_cache_state()
     _check(lib().dit_cache_state_get(handle, ctypes.byref(st)), "dit_cache_state_get")
     return st
+
+
+def dit_cache_factor_get(handle: int, q: int, dst: int, stream: int = 0) -> None:
+    _check(lib().dit_cache_factor_get(handle, q, dst, stream), "dit_cache_factor_get")
 
 
 def dit_denoise_step_cached(handle: int, X: int, ctx: int, ctx_neg: int | None, ctx_len: int,

@@ -847,6 +847,17 @@ dit_status dit_cache_state_get(const dit_model *m, dit_cache_state *out) {
   return DIT_OK;
 }
 
+dit_status dit_cache_factor_get(const dit_model *m, int32_t q, float *dst, void *stream) {
+  if (!m || !ok_ptr(dst)) return DIT_ERR_INVALID_ARG;
+  if (!m->cfg.cache) return DIT_ERR_WORKSPACE;
+  if (m->cache_nb == 0 || q < 0 || q >= m->cache_state.factors) return DIT_ERR_SHAPE;
+  const Plan &p = m->plan;
+  const int64_t n = (int64_t)m->cache_nb * p.S * p.D;
+  const float *tf = m->buf<float>(p.ctf);
+  return hip_status(hipMemcpyAsync(dst, tf + q * n, sizeof(float) * n, hipMemcpyDeviceToDevice,
+                                   static_cast<hipStream_t>(stream)));
+}
+
 dit_status dit_denoise_step_cached(dit_model *m, float *X, const void *ctx, const void *ctx_neg,
                                    int32_t ctx_len, float t, float sigma, float sigma_next,
                                    float guidance_scale, float *v_out, void *stream) {

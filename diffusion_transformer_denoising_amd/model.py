@@ -178,6 +178,13 @@ class DeviceDiT:
         st = B.dit_cache_state_get(self.handle)
         return {n: getattr(st, n) for n, _ in B.dit_cache_state._fields_}
 
+    def cache_factor(self, q: int, nb: int = 1, stream=None) -> torch.Tensor:
+        """Taylor factor q of the current cached run, float [nb, S, D] (a copy)."""
+        out = torch.empty((nb, self.cfg.tokens, self.cfg.hidden), dtype=torch.float32,
+                          device=self.device)
+        B.dit_cache_factor_get(self.handle, q, out.data_ptr(), self._stream(stream))
+        return out
+
     def denoise_step_cached(self, X: torch.Tensor, ctx: torch.Tensor, t: float, sigma: float,
                             sigma_next: float, ctx_neg: torch.Tensor | None = None,
                             guidance_scale: float = 1.0, v_out: torch.Tensor | None = None,

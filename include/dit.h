@@ -280,6 +280,16 @@ dit_status dit_denoise_step_cached(dit_model *model, float *X, const void *ctx,
                                    float sigma_next, float guidance_scale, float *v_out,
                                    void *stream);
 
+/* Diagnostics: enqueue on `stream` a copy of Taylor factor q (0 <= q <
+ * factors in hand, dit_cache_state.factors) of the current cached run into
+ * dst, device float [nb * S * D], nb = 2 for a guided run (positive sequence
+ * first) and 1 otherwise; rows follow the token order.  With TaylorSeer the
+ * cached stand-in is sum_q T_q k^q / q!; this exposes the T_q the last full
+ * step left, so a cached step can be checked against a reference fed the same
+ * factors.  DIT_ERR_WORKSPACE without cache = 1, DIT_ERR_SHAPE for q out of
+ * range or before the first step of a run. */
+dit_status dit_cache_factor_get(const dit_model *model, int32_t q, float *dst, void *stream);
+
 /* Flow Euler update X[i] += (sigma_next - sigma) * v[i] for i < n on device
  * float arrays (layout-agnostic).  n == 0 is a no-op; X and v must be 16-byte
  * aligned, n >= 0.  Page "Model Configuration Conventions", section "Sampling

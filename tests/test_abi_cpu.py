@@ -185,6 +185,7 @@ def test_cache_workspace_and_validation():
     assert L.dit_cache_state_get(None, None) == B.DIT_ERR_INVALID_ARG
     assert L.dit_denoise_step_cached(None, 4096, 4096, None, 1, 1.0, 1.0, 0.0, 1.0, None,
                                      None) == B.DIT_ERR_INVALID_ARG
+    assert L.dit_cache_factor_get(None, 0, 4096, None) == B.DIT_ERR_INVALID_ARG
 
 
 def test_attention_rejects_offsets_past_32_bits():

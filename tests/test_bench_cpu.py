@@ -78,3 +78,50 @@ def test_bench_refuses_more_than_one_gpu(n, capsys):
     b = _bench()
     assert b.main(["--gpus", str(n)]) == 2
     assert "exactly one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("name,unit", [("tiny_f32", "steps"), ("image_s_bf16", "steps"),
+                                       ("wan1p3b_bf16", "block_prefix"),
+                                       ("image_l_bf16", "block"),
+                                       ("wan14b_bf16", "block_prefix")])
+def test_cpu_sample_plan(name, unit):
+    # At 100 GFLOP/s and a 20 s budget: whole steps of the two small
+    # workloads fit, one block of the large image DiT fits, and the video
+    # shapes (a step is hours, a block minutes) get one block on a prefix of
+    # whole grid rows that is the largest one inside the budget.
+    b = _bench()
+    cfg = CONFIGS[name]
+    rate, budget = 1e11, 20.0
+    got, n = b.plan_cpu_sample(cfg, budget, rate)
+    assert got == unit
+    if unit == "block":
+        assert n == cfg.tokens
+    if unit == "block_prefix":
+        row = cfg.grid[2]
+        assert n % row == 0 and row <= n < cfg.tokens
+        assert b.block_flops(cfg, n) / rate <= budget
+        assert b.block_flops(cfg, n + row) / rate > budget
+
+
+def test_block_flops_sum_to_step():
+    # B blocks at the full token count plus the patch, head, text and time
+    # terms make the step's FLOP total
+    b = _bench()
+    for cfg in CONFIGS.values():
+        f = cfg.flops_per_step()
+        extra = 2 * cfg.tokens * cfg.patch_dim * cfg.hidden * 2 + f["time"]
+        if cfg.has_text_proj:
+            extra += 2 * cfg.ctx_len * cfg.text_dim * cfg.hidden
+        assert cfg.num_blocks * b.block_flops(cfg, cfg.tokens) + extra == f["total"]
+
+
+def test_cpu_baseline_block_unit():
+    # A zero budget forces the smallest sample: one block on one grid row.
+    b = _bench()
+    from synth import params as SP
+    cfg = CONFIGS["tiny_f32"]
+    prm = SP.make_params(cfg)
+    r = b.cpu_baseline(cfg, prm, SP.make_latents(cfg), SP.make_ctx(cfg), budget_s=0.0)
+    assert r["kind"] == "oracle" and r["unit"] == "steps/s" and r["value"] > 0
+    assert r["sample_unit"] == "block_prefix" and r["sample_tokens"] == cfg.grid[2]
+    assert f"the first {cfg.grid[2]}" in r["sample"] and r["cores"] >= 1

@@ -1,0 +1,196 @@
+"""Chains at the full video shape and the cached guided run at the pages' knob.
+
+* Full-depth Wan-1.3B model (30 blocks, every block with its own weights):
+  the residual stream is carried through all 30 blocks on the GPU, and blocks
+  0, 15 and 29 are checked teacher-forced (the oracle takes the GPU's input of
+  that block) on sampled rows; the denoise step of the same model is checked
+  on sampled tokens against the head applied to the GPU's last block output.
+* A truncated chain at the real Wan-1.3B sizes: two blocks, two denoise steps
+  of the shifted schedule.  Every block of every step is checked
+  teacher-forced on sampled rows, every step's velocity on sampled tokens, and
+  the latents after both steps against the oracle's two Euler updates
+  accumulated on the same tokens.  (An untruncated float64 chain over all
+  32760 tokens needs the full 32760 x 32760 attention per head and block, far
+  beyond the test's time; the sampled outputs see every token through K and
+  V.)
+* The guided bf16 cached run with the pages' MC = 4: each cached step is
+  recomputed by the oracle from the GPU's latents and the GPU's stored Taylor
+  factors, which isolates the cached step's own arithmetic (probe blocks,
+  stand-in, last block, head) from the amplification of bf16 rounding by the
+  extrapolation weights; the end-to-end error of the same run against the
+  oracle's own cached loop is reported beside it."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from diffusion_transformer_denoising_amd.model import DeviceDiT
+from oracle.cache import CacheKnobs, CachedDenoiser, sample_cached
+from synth import params as SP
+from tests.gpu_helpers import announce, dev_tensor, rel_l2, require_gpu, storage_round, to_np, \
+    tolerances, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows(n, k, seed):
+    rng = np.random.default_rng(seed)
+    r = np.sort(rng.choice(n - 1, k - 1, replace=False))
+    return np.append(r, n - 1)
+
+
+def _sched(cfg, n):
+    sig = oracle.flow_sigmas(cfg.steps, cfg.shift)
+    return [(float(np.float32(1000.0 * sig[i])), float(np.float32(sig[i])),
+             float(np.float32(sig[i + 1]))) for i in range(n)]
+
+
+def _embedded(X0, cfg, g):
+    """Patch-embedded tokens of the latents (oracle, float64) as the float32
+    residual stream handed to the GPU's block calls."""
+    return oracle.linear(oracle.patchify(X0, cfg.patch), g["pe_w"], g["pe_b"]).astype(np.float32)
+
+
+def _check_block(got_rows, x_in, c, mod, p, cfg, pos, rows, what):
+    ref = oracle.dit_block(x_in, c, mod, p, cfg, pos, rows=rows)
+    tol = tolerances(cfg)
+    xr = x_in[rows].astype(np.float64)
+    eb, ed = rel_l2(got_rows, ref), rel_l2(got_rows - xr, ref - xr)
+    print(f"[chain] {what}: block {eb:.2e} update {ed:.2e}", flush=True)
+    assert eb < tol["block"] and ed < tol["delta"], (what, eb, ed)
+    return ref
+
+
+def test_full_depth_blocks_and_step_wan1p3b():
+    require_gpu()
+    cfg = workload("wan1p3b_bf16")
+    announce("full depth wan1p3b", cfg.num_blocks, "blocks")
+    prm = SP.make_params(cfg)
+    g = prm["global"]
+    m = DeviceDiT(cfg, prm)
+    X0 = SP.make_latents(cfg)
+    E = SP.make_ctx(cfg)
+    t, s0, s1 = _sched(cfg, 8)[7]
+    temb, e = oracle.time_embedding(t, g, cfg.freq_dim)
+    c = storage_round(oracle.context_projection(E, g, cfg), cfg.dtype)
+    cd = dev_tensor(c, cfg.dtype)
+    pos = oracle.token_positions(cfg.grid)
+    rows = _rows(cfg.tokens, 24, 41)
+    x = torch.from_numpy(_embedded(X0, cfg, g)).cuda()
+    check = {0, cfg.num_blocks // 2, cfg.num_blocks - 1}
+    for b in range(cfg.num_blocks):
+        mod = oracle.block_modulation(e, prm["blocks"][b]["table"]).astype(np.float32)
+        x_in = to_np(x) if b in check else None
+        m.block_forward(b, x, cd, torch.from_numpy(mod).cuda())
+        torch.cuda.synchronize()
+        if b in check:
+            _check_block(to_np(x)[rows], x_in, c, mod, prm["blocks"][b], cfg, pos, rows,
+                         f"wan1p3b block {b} of {cfg.num_blocks}")
+    # the step of the same model: its velocity at the sampled tokens against
+    # the head on the GPU's own last block output
+    u = oracle.final_layer(to_np(x)[rows], temb, g, cfg)
+    Xd = torch.from_numpy(X0).cuda()
+    v = torch.empty_like(Xd)
+    m.denoise_step(Xd, dev_tensor(E, cfg.dtype), t, s0, s1, v_out=v)
+    torch.cuda.synchronize()
+    ev = rel_l2(oracle.patchify(to_np(v), cfg.patch)[rows], u)
+    ref = oracle.euler_step(oracle.patchify(X0, cfg.patch)[rows], u, s0, s1)
+    ex = rel_l2(oracle.patchify(to_np(Xd), cfg.patch)[rows], ref)
+    print(f"[chain] wan1p3b 30-block step: velocity {ev:.2e} latents {ex:.2e}", flush=True)
+    assert ev < tolerances(cfg)["velocity"] and ex < tolerances(cfg)["latents"]
+
+
+def test_truncated_chain_two_blocks_two_steps_wan1p3b():
+    require_gpu()
+    cfg = workload("wan1p3b_bf16", num_blocks=2)
+    announce("truncated chain wan1p3b 2 blocks x 2 steps")
+    prm = SP.make_params(cfg)
+    g = prm["global"]
+    m = DeviceDiT(cfg, prm)
+    X0 = SP.make_latents(cfg)
+    E = SP.make_ctx(cfg)
+    Ed = dev_tensor(E, cfg.dtype)
+    c = storage_round(oracle.context_projection(E, g, cfg), cfg.dtype)
+    cd = dev_tensor(c, cfg.dtype)
+    pos = oracle.token_positions(cfg.grid)
+    rows = _rows(cfg.tokens, 16, 43)
+    tol = tolerances(cfg)
+    X = torch.from_numpy(X0).cuda()
+    v = torch.empty_like(X)
+    X_acc = oracle.patchify(X0, cfg.patch)[rows]          # oracle latents on the sampled tokens
+    for k, (t, s0, s1) in enumerate(_sched(cfg, 2)):
+        Xk = to_np(X)
+        temb, e = oracle.time_embedding(t, g, cfg.freq_dim)
+        x = torch.from_numpy(_embedded(Xk, cfg, g)).cuda()
+        for b in range(cfg.num_blocks):
+            mod = oracle.block_modulation(e, prm["blocks"][b]["table"]).astype(np.float32)
+            x_in = to_np(x)
+            m.block_forward(b, x, cd, torch.from_numpy(mod).cuda())
+            torch.cuda.synchronize()
+            ref = _check_block(to_np(x)[rows], x_in, c, mod, prm["blocks"][b], cfg, pos, rows,
+                               f"step {k} block {b}")
+        u = oracle.final_layer(ref, temb, g, cfg)
+        m.denoise_step(X, Ed, t, s0, s1, v_out=v)
+        torch.cuda.synchronize()
+        ev = rel_l2(oracle.patchify(to_np(v), cfg.patch)[rows], u)
+        X_acc = oracle.euler_step(X_acc, u, s0, s1)
+        ex = rel_l2(oracle.patchify(to_np(X), cfg.patch)[rows], X_acc)
+        print(f"[chain] step {k}: velocity {ev:.2e} latents {ex:.2e}", flush=True)
+        assert ev < tol["velocity"] and ex < tol["latents"], (k, ev, ex)
+
+
+def test_guided_cached_run_at_the_pages_knobs_bf16():
+    require_gpu()
+    knobs = dict(fn=2, bn=1, warmup=4, rdt=float("inf"), max_consecutive=4, taylorseer=True,
+                 ts_order=2)
+    cfg = workload("image_s_bf16", latent=(1, 8, 12), num_blocks=5)
+    announce("guided cached bf16 MC=4", cfg.tokens, cfg.num_blocks)
+    prm = SP.make_params(cfg)
+    for p in prm["blocks"]:
+        p["co_w"] = storage_round(p["co_w"] * 25.0, cfg.dtype)
+    X0 = SP.make_latents(cfg)
+    E, En = SP.make_ctx(cfg), SP.make_ctx(cfg, seed=3)
+    sched = _sched(cfg.with_(steps=14), 14)
+    m = DeviceDiT(cfg, prm, guidance=True, cache=True)
+    m.cache_begin(**knobs)
+    X = torch.from_numpy(X0).cuda()
+    v = torch.empty_like(X)
+    Ed, End = dev_tensor(E, cfg.dtype), dev_tensor(En, cfg.dtype)
+    ok = CacheKnobs(**knobs)
+    gpu, forced = [], []
+    for i, (t, s0, s1) in enumerate(sched):
+        before = m.cache_state()
+        Xk = to_np(X)
+        facs = ([to_np(m.cache_factor(q, nb=2)) for q in range(before["factors"])]
+                if before["factors"] else [])
+        m.denoise_step_cached(X, Ed, t, s0, s1, ctx_neg=End, guidance_scale=4.0, v_out=v)
+        torch.cuda.synchronize()
+        st = m.cache_state()
+        gpu.append(bool(st["hit"]))
+        if st["hit"]:
+            # the oracle's cached step from the GPU's latents and factors
+            den = CachedDenoiser(prm, cfg, ok)
+            pol = den.policy
+            pol.step, pol.last_full = before["step"], before["last_full"]
+            pol.consecutive, pol.factors = before["consecutive"], before["factors"]
+            den.factors = [[f[n] for f in facs] for n in range(2)]
+            den.p_ref = np.zeros((2 * cfg.tokens, cfg.hidden))
+            _, Vo, hit, _ = den.step(Xk, [E, En], t, s0, s1, 4.0, force=True)
+            assert hit
+            forced.append((i, st["step"] - 1 - before["last_full"], rel_l2(to_np(v), Vo)))
+    assert max(k for _, k, _ in forced) == 4, forced   # a fourth cached step in a row ran
+    print("[cache] hits", gpu, flush=True)
+    print("[cache] cached step from the GPU's factors: " +
+          ", ".join(f"step {i} (k={k}) {e:.2e}" for i, k, e in forced), flush=True)
+    assert max(e for _, _, e in forced) < tolerances(cfg)["velocity"]
+    # end to end against the oracle's own cached loop (same decisions)
+    ref = sample_cached(X0, [E, En], prm, cfg, ok, sched, 4.0, force=gpu)
+    m.cache_begin(**knobs)
+    X.copy_(torch.from_numpy(X0))
+    ee = []
+    for i, (t, s0, s1) in enumerate(sched):
+        m.denoise_step_cached(X, Ed, t, s0, s1, ctx_neg=End, guidance_scale=4.0, v_out=v)
+        torch.cuda.synchronize()
+        ee.append(rel_l2(to_np(v), ref[i][1]))
+    print("[cache] end to end velocity error: " +
+          ", ".join(f"{e:.2e}{'*' if h else ''}" for e, h in zip(ee, gpu)), flush=True)

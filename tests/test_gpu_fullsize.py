@@ -72,7 +72,8 @@ def _block_full(cfg, rows, mode):
 
 
 @pytest.mark.parametrize("name,mode", [("wan1p3b_bf16", "time-mod"), ("wan1p3b_bf16", "sharp"),
-                                       ("image_l_bf16", "time-mod")])
+                                       ("image_l_bf16", "time-mod"), ("wan14b_bf16", "time-mod"),
+                                       ("wan14b_bf16", "sharp")])
 def test_block_full_size(name, mode):
     require_gpu()
     cfg = workload(name)
@@ -106,13 +107,16 @@ def test_block_zero_gates_identity_wan14b():
     assert torch.equal(x, x0)
 
 
-def test_denoise_step_one_block_full_size():
-    """One denoise step of the Wan-1.3B shape with one block (text projection
-    4096 -> 1536, patch embed, block, head, unpatchify + Euler), velocity and
-    latents compared at every latent element of sampled tokens."""
+@pytest.mark.parametrize("name", ["wan1p3b_bf16", "image_l_bf16"])
+def test_denoise_step_one_block_full_size(name):
+    """One denoise step with one block at full size (Wan-1.3B: text
+    projection 4096 -> 1536; large image DiT: 4096 tokens of width 3584, 1024
+    context tokens, no projection), patch embed, block, head, unpatchify +
+    Euler; velocity and latents compared at every latent element of sampled
+    tokens."""
     require_gpu()
-    cfg = workload("wan1p3b_bf16", num_blocks=1)
-    announce("step full wan1p3b 1 block")
+    cfg = workload(name, num_blocks=1)
+    announce("step full 1 block", name)
     prm = SP.make_params(cfg)
     m = DeviceDiT(cfg, prm)
     X0 = SP.make_latents(cfg)
