@@ -198,7 +198,10 @@ def cpu_baseline(cfg, prm, X0, E, budget_s: float = 20.0, E_neg=None, g=None) ->
     cores = _host_threads()
     step_flops = cfg.flops_per_step()["total"] * (2 if E_neg is not None else 1)
     rate = host_matmul_rate()
-    unit, n = plan_cpu_sample(cfg, budget_s, 0.5 * rate * (2 if E_neg is not None else 1))
+    # the oracle's block reaches ~18 % of the host's large-matmul rate at the
+    # Wan-14B width (its attention is elementwise numpy over S x S scores), so
+    # the sample is sized at 15 % of it
+    unit, n = plan_cpu_sample(cfg, budget_s, 0.15 * rate / (2 if E_neg is not None else 1))
     sig = oracle.flow_sigmas(cfg.steps, cfg.shift)
     if unit == "steps":
         X = X0.astype(np.float64)

@@ -29,11 +29,10 @@ namespace dit {
 
 constexpr int ATT_BQ = 128;  // queries per workgroup (4 waves x 32)
 
-// Problem blockIdx.z of a batched launch: its operands start at the batch
-// strides (elements of size es) from the first problem's.
-__device__ __forceinline__ void att_select_batch(AttnArgs &p, int es) {
+// Problem z of a batched launch: its operands start at the batch strides
+// (elements of size es) from the first problem's.
+__device__ __forceinline__ void att_select_batch(AttnArgs &p, int es, int64_t z) {
   if (p.batch > 1) {
-    const int64_t z = blockIdx.z;
     p.q = static_cast<const char *>(p.q) + z * p.bq * es;
     p.k = static_cast<const char *>(p.k) + z * p.bk * es;
     p.vt = static_cast<const char *>(p.vt) + z * p.bvt * es;
@@ -71,7 +70,7 @@ __device__ __forceinline__ void load4_into(typename Frag<T>::type &f, int s, con
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attention_kernel(AttnArgs p) {
-  att_select_batch(p, sizeof(T));
+  att_select_batch(p, sizeof(T), blockIdx.z);
   typedef typename Frag<T>::type F;
   constexpr int VEC = 16 / sizeof(T);
   constexpr int KROW = HD + VEC;          // K tile row stride (16-byte pad)
@@ -353,7 +352,15 @@ __device__ __forceinline__ void att_exp_half(const f32x16 &x, bf16x8 &lo, bf16x8
 
 template <int HD, int NW, int KS = 1>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kernel(AttnArgs p) {
-  att_select_batch(p, 2);
+  // XCD-aware order: the query blocks of one head (and the heads of one
+  // problem) are consecutive logical indices, and every XCD takes one
+  // contiguous range of them, so an XCD's L2 fetches the K and V^T of the few
+  // heads it works on rather than of every head.
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int wg = xcd_contiguous(blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z),
+                                gx * gy * gridDim.z);
+  const int bx = wg % gx, by = (wg / gx) % gy, bz = wg / (gx * gy);
+  att_select_batch(p, 2, bz);
   typedef bf16x8 F;
   constexpr int KROWB = HD * 2;            // bytes per K row
   constexpr int KCHUNK = KROWB / 16;       // 16-byte chunks per K row
@@ -386,8 +393,8 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kerne
   const int grp = wave / NWG, wig = wave % NWG;  // key range, wave within it
   const int rbase = grp * RING;                  // LDS ring of this key range
   const int half = lane >> 5, l32 = lane & 31;
-  const int head = blockIdx.y;
-  const int q0 = blockIdx.x * (32 * NWG) + wig * 32;
+  const int head = by;
+  const int q0 = bx * (32 * NWG) + wig * 32;
   const int sq = p.sq, sk = p.sk;
   const bf16 *Q = static_cast<const bf16 *>(p.q) + head * HD;
 

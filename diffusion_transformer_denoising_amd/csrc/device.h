@@ -90,6 +90,16 @@ __device__ __forceinline__ void dma_to_lds16(i32x4 rsrc, uint32_t lds_addr, uint
                :: "v"(voff), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
+// Workgroups are handed to the chip's 8 XCDs round-robin by linear id (id % 8),
+// and each XCD has its own L2.  This maps the linear id of a grid of n
+// workgroups to a logical index so that every XCD gets one contiguous range
+// of logical indices (the first n % 8 XCDs one more than the rest), walked in
+// dispatch order.
+__device__ __forceinline__ int xcd_contiguous(int id, int n) {
+  const int xcd = id & 7, local = id >> 3, per = n >> 3, rem = n & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // GELU, tanh form: z/2 (1 + tanh(u)) with u = sqrt(2/pi) (z + 0.044715 z^3),

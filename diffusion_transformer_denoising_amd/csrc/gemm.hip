@@ -320,9 +320,7 @@ struct GemmEpilogue {
 __device__ __forceinline__ void gemm_tile_of(int nx, int ny, int &tm, int &tn) {
   constexpr int GM = 4;
   const int T = nx * ny;
-  const int id = blockIdx.x;
-  const int xcd = id & 7, local = id >> 3;
-  const int t = xcd * (T >> 3) + (xcd < (T & 7) ? xcd : (T & 7)) + local;
+  const int t = xcd_contiguous(blockIdx.x, T);
   const int gsz = GM * nx;                       // tiles per group of GM rows
   const int g = t / gsz, r = t - g * gsz;
   const int rows = ny - g * GM < GM ? ny - g * GM : GM;  // rows in this (last) group
