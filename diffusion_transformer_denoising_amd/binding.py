@@ -79,6 +79,8 @@ _SIGS = {
                     c_vp, ctypes.POINTER(c_vp)], c_i32),
     "dit_destroy": ([c_vp], c_i32),
     "dit_block_forward": ([c_vp, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp], c_i32),
+    "dit_block_forward_static": ([ctypes.POINTER(dit_config), ctypes.POINTER(dit_block_weights),
+                                  c_vp, c_vp, c_i32, c_vp, c_vp], c_i32),
     "dit_denoise_step": ([c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_f32, c_vp, c_vp], c_i32),
     "dit_denoise_step_cfg": ([c_vp, c_vp, c_vp, c_vp, c_i32, c_f32, c_f32, c_f32, c_f32, c_vp,
                               c_vp], c_i32),
@@ -217,6 +219,12 @@ def dit_cache_state_get(handle: int) -> dit_cache_state:
     st = dit_cache_state()
     _check(lib().dit_cache_state_get(handle, ctypes.byref(st)), "dit_cache_state_get")
     return st
+
+
+def dit_block_forward_static(cfg: dit_config, weights: dit_block_weights, x: int, ctx: int,
+                             ctx_len: int, mod: int, stream: int = 0) -> None:
+    _check(lib().dit_block_forward_static(ctypes.byref(cfg), ctypes.byref(weights), x, ctx,
+                                          ctx_len, mod, stream), "dit_block_forward_static")
 
 
 def dit_cache_factor_get(handle: int, q: int, dst: int, stream: int = 0) -> None:

@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -554,6 +555,70 @@ dit_status dit_create(const dit_config *cfg, const dit_weights *weights, void *w
 dit_status dit_destroy(dit_model *model) {
   delete model;
   return DIT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Library-owned scratch of dit_block_forward_static, one copy per device (the
+// code object's own global).  In host code `scratch` names a host-side stand-in,
+// never the device memory: kernels and copies get the address that
+// hipGetSymbolAddress returns for the current device, kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[DIT_STATIC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[kMaxDevices] = {};
+
+// The device address of the scratch array on the current device, looked up
+// once per device with that device current; nullptr on failure.
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+dit_status dit_block_forward_static(const dit_config *cfg, const dit_block_weights *w, float *x,
+                                    const void *ctx, int32_t ctx_len, const float *mod,
+                                    void *stream) {
+  dit_status st = check_config(cfg);
+  if (st != DIT_OK) return st;
+  if (cfg->guidance || cfg->offload || cfg->cache) return DIT_ERR_UNSUPPORTED;
+  if (!w || !ok_ptr(x) || !ok_ptr(ctx) || !ok_ptr(mod)) return DIT_ERR_INVALID_ARG;
+  if ((st = check_block(*w)) != DIT_OK) return st;
+  if (ctx_len < 1 || ctx_len > cfg->ctx_len_max) return DIT_ERR_SHAPE;
+  // the plan of a one-block model: rotary tables, activations, one block's
+  // cross K / V^T
+  dit_config one = *cfg;
+  one.num_blocks = 1;
+  Plan p;
+  plan_layout(one, p);
+  if (p.total > DIT_STATIC_SCRATCH_BYTES) return DIT_ERR_WORKSPACE;
+  char *ws = static_cast<char *>(scratch_on_current_device());
+  if (!ws) return DIT_ERR_HIP;
+  // a handle on the stack: no heap memory, profiling off, no offload or cache
+  dit_model m;
+  m.cfg = one;
+  m.dt = one.dtype == DIT_BF16 ? DT_BF16 : DT_F32;
+  m.ws = ws;
+  m.plan = p;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DIT_TRY(launch_rope_tables(m.buf<float>(p.cos_t), m.buf<float>(p.sin_t),
+                             one.lat_f / one.patch_f, one.lat_h / one.patch_h,
+                             one.lat_w / one.patch_w, one.head_dim, one.rope_f, one.rope_h,
+                             one.rope_w, one.rope_theta, s));
+  const void *ctxs[1] = {ctx};
+  return run_block(&m, *w, 0, x, ctxs, ctx_len, mod, s, false, 1);
 }
 
 dit_status dit_block_forward(dit_model *m, int32_t block, float *x, const void *ctx,

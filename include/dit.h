@@ -188,6 +188,27 @@ dit_status dit_destroy(dit_model *model);
 dit_status dit_block_forward(dit_model *model, int32_t block, float *x, const void *ctx,
                              int32_t ctx_len, const float *mod, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the block of
+ * dit_block_forward without a handle or a workspace.  Arguments as there, with
+ * the configuration and this block's weights (device pointers) passed
+ * directly; cfg->num_blocks is ignored, and guidance, offload and cache must
+ * be 0 (else DIT_ERR_UNSUPPORTED).  The rotary tables and every intermediate
+ * buffer (LayerNorm output, q, k, transposed values, attention output, MLP
+ * hidden, cross K / V^T) live in a library-owned device array of
+ * DIT_STATIC_SCRATCH_BYTES, one per device, held until the process ends; a
+ * configuration whose one-block workspace (dit_workspace_size with
+ * num_blocks = 1) exceeds it is refused with DIT_ERR_WORKSPACE before any
+ * device work.  The call allocates nothing (no hipMalloc or hipFree, no heap
+ * memory).  Every call on a device shares that device's array and leaves its
+ * last contents there; nothing in it needs to start at zero.  Calls that
+ * overlap on one device (concurrent streams or threads) race on the array and
+ * must be serialised by the caller. */
+#define DIT_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+dit_status dit_block_forward_static(const dit_config *cfg, const dit_block_weights *weights,
+                                    float *x, const void *ctx, int32_t ctx_len, const float *mod,
+                                    void *stream);
+
 /* One denoising step: velocity V = DiT(X, ctx, t), then X += (sigma_next -
  * sigma) * V.
  *   X      device float [C, F, H, W] latents, read and overwritten;
