@@ -984,7 +984,7 @@ dit_status dit_gemm(int32_t dtype, int32_t epilogue, const void *A, int64_t lda,
   if (epilogue < DIT_EPI_STORE || epilogue > DIT_EPI_STORE_F32) return DIT_ERR_INVALID_ARG;
   if (!ok_ptr(A) || !ok_ptr(W) || !ok_ptr(out)) return DIT_ERR_INVALID_ARG;
   if ((bias && !aligned16(bias)) || (gate && !aligned16(gate))) return DIT_ERR_INVALID_ARG;
-  if (tile < 0 || tile > 4) return DIT_ERR_INVALID_ARG;
+  if (tile < 0 || tile > 5) return DIT_ERR_INVALID_ARG;
   if (M < 1 || N < 1 || K < 1 || lda < K || ldw < K || ldo < N) return DIT_ERR_SHAPE;
   if ((K | lda | ldw) & 7) return DIT_ERR_UNSUPPORTED;
   if (!gemm_offsets_fit(dtype == DIT_BF16 ? DT_BF16 : DT_F32, M, lda, N, ldw))

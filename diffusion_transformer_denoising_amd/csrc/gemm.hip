@@ -72,10 +72,16 @@ constexpr int gemm_strip_floats() {
 }
 
 // NWN waves along N, NW waves in all (NW / NWN along M); each wave owns a
-// WM x WN block as TM x TN 32x32 accumulators.
-template <typename T, int BM, int BN, int EPI, int NWN = 2, int NW = 4, bool PRE = false>
+// WM x WN block, as TM x TN 32x32 accumulators (CW = 32: lane = column of a
+// 32-column block, rows j*8 + (lane/32)*4 + i) or as (2 TM) x (2 TN) 16x16
+// accumulators (CW = 16: lane % 16 = column of a 16-column block, rows
+// (lane/16)*4 + i of a 16-row block).
+template <typename T, int BM, int BN, int EPI, int NWN = 2, int NW = 4, bool PRE = false,
+          int CW = 32>
 struct GemmEpilogue {
   static constexpr int WM = BM * NWN / NW, WN = BN / NWN, TM = WM / 32, TN = WN / 32;
+  static constexpr int NCB = WN / CW;                        // column blocks per wave
+  static_assert(CW == 32 || CW == 16, "accumulator layouts");
   static constexpr int SROW = WN + 4;                        // fp32 strip row stride
   static constexpr int TROW = 32 + 16 / (int)sizeof(T);      // transposed strip row stride
   static constexpr int REG = gemm_strip_floats<T, WN>();
@@ -90,8 +96,8 @@ struct GemmEpilogue {
   void *dst;
   int64_t ld;
   bool vec_ok;
-  uint32_t bw[TN];  // bias bits (bf16 in the low half, or fp32) until used
-  float gv[TN];
+  uint32_t bw[NCB];  // bias bits (bf16 in the low half, or fp32) until used
+  float gv[NCB];
   f32x4 pre[PRE ? TM : 1][NIT][2];  // per strip with PRE, else the current strip's
 
   __device__ __forceinline__ GemmEpilogue(const GemmArgs &args, int m0_, int n0,
@@ -120,7 +126,7 @@ struct GemmEpilogue {
     vec_ok = (ld % VE) == 0;
   }
 
-  // bias and gate of the lane's column in each 32-column block, by raw buffer
+  // bias and gate of the lane's column in each CW-column block, by raw buffer
   // loads: past column N, and for a missing operand (an empty range), they
   // return zero without a branch; the bias stays raw bits until it is used, so
   // nothing waits for these loads where they are issued
@@ -130,8 +136,8 @@ struct GemmEpilogue {
     const auto gr = make_rsrc(EPI == EPI_RESIDUAL && p.gate ? static_cast<const void *>(p.gate) : p.A,
                               EPI == EPI_RESIDUAL && p.gate ? (uint32_t)(N * 4) : 0u);
 #pragma unroll
-    for (int b = 0; b < TN; ++b) {
-      const uint32_t col = (uint32_t)(colbase + b * 32 + (lane & 31));
+    for (int b = 0; b < NCB; ++b) {
+      const uint32_t col = (uint32_t)(colbase + b * CW + (lane & (CW - 1)));
       if constexpr (sizeof(T) == 2)
         bw[b] = __builtin_amdgcn_raw_buffer_load_b16(br, col * 2, 0, 0);
       else
@@ -179,9 +185,40 @@ struct GemmEpilogue {
     for (int a = 0; a < TM; ++a) load_runs(a, pre[a]);
   }
 
+  // Four consecutive rows r0 .. r0+3 of strip column sc, column block b:
+  // bias, GELU or gate applied, into the strip (transposed for a transposed
+  // segment).
+  __device__ __forceinline__ void put4(float *strip, T *stripT, int sc, int r0, int b,
+                                       const float (&a)[4]) {
+    const float bv = __uint_as_float(sizeof(T) == 2 ? bw[b] << 16 : bw[b]);
+    const float gb = EPI == EPI_RESIDUAL && p.gate ? gv[b] : 1.0f;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i] + bv;
+      if constexpr (EPI == EPI_GELU) v[i] = gelu_tanh(v[i]);
+      if constexpr (EPI == EPI_RESIDUAL) v[i] *= gb;
+    }
+    if (EPI == EPI_SPLIT && trans) {
+      if constexpr (sizeof(T) == 2) {
+        bf16x4 t4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t4[i] = (bf16)v[i];
+        *reinterpret_cast<bf16x4 *>(stripT + sc * TROW + r0) = t4;
+      } else {
+        *reinterpret_cast<f32x4 *>(stripT + sc * TROW + r0) = f32x4{v[0], v[1], v[2], v[3]};
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) strip[(r0 + i) * SROW + sc] = v[i];
+    }
+  }
+
   // The caller has synchronised the workgroup: scratch is free LDS of at
-  // least NW * REG floats.
-  __device__ __forceinline__ void store(f32x16 (&acc)[TM][TN], float *scratch) {
+  // least NW * REG floats.  acc is f32x16[TM][TN] (CW = 32) or
+  // f32x4[2 TM][2 TN] (CW = 16).
+  template <typename ACC>
+  __device__ __forceinline__ void store(ACC &acc, float *scratch) {
     float *strip = scratch + wave * REG;
     T *stripT = reinterpret_cast<T *>(strip);
     if constexpr (!PRE) load_cols();
@@ -189,35 +226,24 @@ struct GemmEpilogue {
     for (int a = 0; a < TM; ++a) {
       const int rowbase = m0 + wm * WM + a * 32;
       // 1. accumulators -> strip
+      if constexpr (CW == 32) {
 #pragma unroll
-      for (int b = 0; b < TN; ++b) {
-        const int sc = b * 32 + (lane & 31);
-        const float bv = __uint_as_float(sizeof(T) == 2 ? bw[b] << 16 : bw[b]);
-        const float gb = EPI == EPI_RESIDUAL && p.gate ? gv[b] : 1.0f;
+        for (int b = 0; b < TN; ++b)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r0 = j * 8 + (lane >> 5) * 4;
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[i] = acc[a][b][j * 4 + i] + bv;
-            if constexpr (EPI == EPI_GELU) v[i] = gelu_tanh(v[i]);
-            if constexpr (EPI == EPI_RESIDUAL) v[i] *= gb;
+          for (int j = 0; j < 4; ++j) {
+            const float v[4] = {acc[a][b][j * 4], acc[a][b][j * 4 + 1], acc[a][b][j * 4 + 2],
+                                acc[a][b][j * 4 + 3]};
+            put4(strip, stripT, b * 32 + (lane & 31), j * 8 + (lane >> 5) * 4, b, v);
           }
-          if (EPI == EPI_SPLIT && trans) {
-            if constexpr (sizeof(T) == 2) {
-              bf16x4 t4;
+      } else {
 #pragma unroll
-              for (int i = 0; i < 4; ++i) t4[i] = (bf16)v[i];
-              *reinterpret_cast<bf16x4 *>(stripT + sc * TROW + r0) = t4;
-            } else {
-              *reinterpret_cast<f32x4 *>(stripT + sc * TROW + r0) = f32x4{v[0], v[1], v[2], v[3]};
-            }
-          } else {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) strip[(r0 + i) * SROW + sc] = v[i];
+          for (int b = 0; b < NCB; ++b) {
+            const f32x4 &c = acc[2 * a + t][b];
+            const float v[4] = {c[0], c[1], c[2], c[3]};
+            put4(strip, stripT, b * 16 + (lane & 15), t * 16 + (lane >> 4) * 4, b, v);
           }
-        }
       }
       wave_lds_sync();
       // 2. strip -> global, 8-element runs
@@ -502,6 +528,167 @@ __global__ __launch_bounds__(64 * NW) void gemm_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Register-staged main loop on 16x16x32 MFMAs (bf16, 256x256, 8 waves).
+// Same slice staging, LDS layout (128-byte rows + 16 bytes of padding) and
+// one barrier per 64-k slice as gemm_kernel, but each slice is two 32-k
+// chunks of v_mfma_f32_16x16x32_bf16, and a wave's WM x WN block is
+// (WM/16) x (WN/16) 16x16 accumulators.  A fragment (16 bytes per lane) now
+// covers 16 rows x 32 k, so a chunk needs twice the fragments of a 32x32x16
+// chunk; to keep the register count, the W fragments are double-buffered
+// across chunks while the A fragments stream through a ring of four: A
+// fragment a + 4 (or, past the chunk's last, fragment a - 4 of the next
+// chunk) is read as soon as the MFMAs of fragment a have been issued.
+// Lane layout of the instruction: A and B lanes l hold row l % 16, k
+// (l / 16) * 8 .. + 7; the accumulator lane l holds rows (l / 16) * 4 + i of
+// column l % 16.
+// ---------------------------------------------------------------------------
+template <int EPI, int NWN = 4, int NW = 8>
+__global__ __launch_bounds__(64 * NW) void gemm16_kernel(GemmArgs p) {
+  typedef bf16 T;
+  constexpr int BM = 256, BN = 256, NT = 64 * NW;
+  constexpr int BK = 64, VEC = 8, ROW = BK + VEC, CHUNKS = BK / 32;
+  // 8 waves: 128 x 64 per wave as 8 x 4 accumulators.  (4 waves of 128 x 128,
+  // one wave per SIMD with the accumulators in AGPRs, also fit this code; they
+  // were 16-27 % slower on the step shapes.)
+  constexpr int WM = BM * NWN / NW, WN = BN / NWN;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int RING = 4;
+  static_assert(TM == 2 * RING, "the A ring covers half a chunk");
+  constexpr int RPP = NT / 8, LA = BM / RPP, LW = BN / RPP, NP = LA + LW;
+  // per A fragment: staging pieces moved in chunk 0, and (from fragment RING
+  // on, i.e. after the last chunk's barrier) W fragments of the next chunk read
+  constexpr int SPER = NP / TM, WPER = TN / (TM - RING);
+  static_assert(SPER * TM == NP && WPER * (TM - RING) == TN, "schedule shares");
+  __shared__ __attribute__((aligned(16))) T lds[2][(BM + BN) * ROW];
+  static_assert(NW * gemm_strip_floats<T, WN>() * 4 <= (int)sizeof(lds), "epilogue strips");
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int M = p.M, N = p.N, K = p.K;
+  int tm, tn;
+  gemm_tile_of((N + BN - 1) / BN, (M + BM - 1) / BM, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int kk = (tid & 7) * VEC, r0 = tid >> 3;
+  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(p.A, (uint32_t)((int64_t)M * p.lda * 2));
+  const void *Wg, *bias_g;
+  int g;
+  gemm_group(p, Wg, bias_g, g);
+  const __amdgpu_buffer_rsrc_t rw_src = make_rsrc(Wg, (uint32_t)((int64_t)N * p.ldw * 2));
+  const uint32_t a_off0 = (uint32_t)(((int64_t)(m0 + r0) * p.lda + kk) * 2);
+  const uint32_t w_off0 = (uint32_t)(((int64_t)(n0 + r0) * p.ldw + kk) * 2);
+  const uint32_t a_step = (uint32_t)(RPP * p.lda * 2), w_step = (uint32_t)(RPP * p.ldw * 2);
+
+  U128 stage[NP];
+  auto gload_piece = [&](int i, int kt) {
+    const int k0 = kt * BK;
+    const bool kin = (k0 + kk) < K;
+    const uint32_t kb = (uint32_t)(k0 * 2);
+    if (i < LA)
+      stage[i] = buf_load16(ra_src, kin ? a_off0 + i * a_step + kb : OOB);
+    else
+      stage[i] = buf_load16(rw_src, kin ? w_off0 + (i - LA) * w_step + kb : OOB);
+  };
+  auto sstore_piece = [&](int i, T *base) {
+    const int row = i < LA ? r0 + RPP * i : BM + r0 + RPP * (i - LA);
+    *reinterpret_cast<U128 *>(base + row * ROW + kk) = stage[i];
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int arow = (wm * WM + (lane & 15)) * ROW + (lane >> 4) * 8;
+  const int wrow = (BM + wn * WN + (lane & 15)) * ROW + (lane >> 4) * 8;
+  bf16x8 ar[RING], wf[2][TN];
+  auto afrag = [&](const T *base, int ch, int a) {
+    return *reinterpret_cast<const bf16x8 *>(base + arow + a * 16 * ROW + ch * 32);
+  };
+  auto wfrag = [&](const T *base, int ch, int b) {
+    return *reinterpret_cast<const bf16x8 *>(base + wrow + b * 16 * ROW + ch * 32);
+  };
+
+  const int KT = (K + BK - 1) / BK;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) gload_piece(i, 0);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) sstore_piece(i, lds[0]);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) gload_piece(i, 1);
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < RING; ++a) ar[a] = afrag(lds[0], 0, a);
+#pragma unroll
+  for (int b = 0; b < TN; ++b) wf[0][b] = wfrag(lds[0], 0, b);
+
+  // Chunk 0 of a step moves every staging piece (slice kt+1 into the other
+  // buffer, then slice kt+2 into the registers).  In the last chunk, the
+  // ring reads of the current buffer come first (fragments 0 .. RING-1 of the
+  // chunk are already in the ring), then the one barrier of the step, after
+  // which slice kt+1 is in the other buffer for every wave and the current
+  // buffer is no longer read by any wave (so the next step may overwrite it);
+  // the next slice's first fragments are read after it.  The step body is
+  // branch-free: past the last slice the loads fall out of range and return
+  // zero.
+  for (int kt = 0; kt < KT; ++kt) {
+    const T *base = lds[kt & 1];
+    T *next = lds[(kt & 1) ^ 1];
+    static_for<CHUNKS>([&](auto CH) {
+      constexpr int ch = CH;
+      constexpr int slot = ch & 1;
+      constexpr bool last = ch + 1 == CHUNKS;
+      const T *nb = last ? next : base;   // buffer of the next chunk
+      constexpr int nch = last ? 0 : ch + 1;
+      static_for<TM>([&](auto A) {
+        constexpr int a = A;
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar[a % RING], wf[slot][b], acc[a][b],
+                                                              0, 0, 0);
+        // refill the ring slot just used; the next chunk's W fragments
+        if constexpr (a + RING < TM) ar[a % RING] = afrag(base, ch, a + RING);
+        else ar[a % RING] = afrag(nb, nch, a + RING - TM);
+        constexpr int NWR = a >= RING ? WPER : 0;
+#pragma unroll
+        for (int j = 0; j < NWR; ++j)
+          wf[slot ^ 1][(a - RING) * WPER + j] = wfrag(nb, nch, (a - RING) * WPER + j);
+        if constexpr (ch == 0) {
+#pragma unroll
+          for (int j = 0; j < SPER; ++j) {
+            sstore_piece(a * SPER + j, next);
+            gload_piece(a * SPER + j, kt + 2);
+          }
+        }
+        // MFMAs with the ring read, the W reads and the staging stores +
+        // loads between them, in that order
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        static_for<NWR>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+        constexpr int NST = ch == 0 ? SPER : 0;
+        static_for<NST>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        });
+        constexpr int REST = TN - 1 - NWR - NST;
+        if constexpr (REST > 0) __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (last && a == RING - 1) __syncthreads();
+      });
+    });
+  }
+
+  __syncthreads();
+  GemmEpilogue<T, BM, BN, EPI, NWN, NW, false, 16>(p, m0, n0, bias_g, g)
+      .store(acc, reinterpret_cast<float *>(&lds[0][0]));
+}
+
+// ---------------------------------------------------------------------------
 // Direct-to-LDS main loop with an NS-stage ring (bf16, BM x BN up to 128).
 // Stage layout: BM rows of A then BN rows of W, 128 bytes (64 k) each; the
 // 16-byte chunk c of row r is stored at chunk c ^ ((r >> 1) & 7), which makes
@@ -674,6 +861,21 @@ static hipError_t launch_t(Epilogue epi, const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NWN, int NW>
+static hipError_t launch_16(Epilogue epi, const GemmArgs &a, hipStream_t s) {
+  dim3 grid(((a.N + 255) / 256) * ((a.M + 255) / 256), a.gw ? a.groups : 1);
+  constexpr int NT = 64 * NW;
+  switch (epi) {
+    case EPI_STORE: dit_launch(gemm16_kernel<EPI_STORE, NWN, NW>, grid, NT, s, a); break;
+    case EPI_GELU: dit_launch(gemm16_kernel<EPI_GELU, NWN, NW>, grid, NT, s, a); break;
+    case EPI_RESIDUAL: dit_launch(gemm16_kernel<EPI_RESIDUAL, NWN, NW>, grid, NT, s, a); break;
+    case EPI_STORE_F32: dit_launch(gemm16_kernel<EPI_STORE_F32, NWN, NW>, grid, NT, s, a); break;
+    case EPI_SPLIT: dit_launch(gemm16_kernel<EPI_SPLIT, NWN, NW>, grid, NT, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int NS>
 static hipError_t launch_dl(Epilogue epi, const GemmArgs &a, hipStream_t s) {
   dim3 grid(((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM), a.gw ? a.groups : 1);
@@ -695,8 +897,10 @@ bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) 
 }
 
 // Tile choice (measured on MI355X): 256x256 with 8 waves (two per SIMD, 3-15%
-// faster than 4 waves on every large step shape) once the grid has at least
-// half a tile per CU; else 64x64.  Below that size 64x64 beat 128x128
+// faster than 4 waves on every large step shape) on 16x16x32 MFMAs (0-3 %
+// faster than the same tile on 32x32x16 on the large step shapes, never
+// slower beyond noise) once the grid has at least half a tile per CU; else
+// 64x64.  Below that size 64x64 beat 128x128
 // everywhere it was timed: MLP-1 at 1024 tokens (768 tiles, 11.0 against
 // 12.0 us), and, once the 64x64 epilogue read its operands ahead, the grouped
 // cross K/V projection at 1024 tokens (1152 tiles) and the guided step's QKV
@@ -705,7 +909,7 @@ bool gemm_offsets_fit(DType dt, int64_t M, int64_t lda, int64_t N, int64_t ldw) 
 static int pick_tile(int M, int N, int groups) {
   const int64_t G = groups > 1 ? groups : 1;
   const int64_t t256 = G * ((M + 255) / 256) * ((N + 255) / 256);
-  return t256 >= 128 ? 4 : 3;
+  return t256 >= 128 ? 5 : 3;
 }
 
 hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s, int tile) {
@@ -719,9 +923,11 @@ hipError_t launch_gemm(DType dt, Epilogue epi, const GemmArgs &a, hipStream_t s,
     // columns for tile 1, 64 for tiles 2 and 4, 32 for tile 3
     if (epi == EPI_SPLIT && tile == 1 && a.seg_width % 128 != 0) tile = 4;
     if (epi == EPI_SPLIT && tile != 3 && a.seg_width % 64 != 0) tile = 3;
+    if (epi == EPI_SPLIT && tile == 5 && a.seg_width % 64 != 0) tile = 3;
     switch (tile) {
       case 1: return launch_t<bf16, 256, 256>(epi, a, s);
       case 4: return launch_t<bf16, 256, 256, 4, 8>(epi, a, s);
+      case 5: return launch_16<4, 8>(epi, a, s);
       case 2: return launch_dl<128, 128, 4>(epi, a, s);
       default: {
         // 5 stages (80 KB of LDS, two workgroups per CU) unless the grid has

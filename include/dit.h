@@ -359,8 +359,9 @@ dit_status dit_attention(int32_t dtype, int32_t heads, int32_t head_dim, const v
  * A device T [M, lda], W device T [N, ldw], bias device T [N] or NULL.
  * M, N, K >= 1; K, lda and ldw multiples of 8; lda, ldw >= K;
  * ldo >= N.  tile selects the workgroup tile (0 automatic, 1: 256x256 with
- * 4 waves, 2: 128x128, 3: 64x64, 4: 256x256 with 8 waves; fp32 always uses
- * 64x64); other values give DIT_ERR_INVALID_ARG. */
+ * 4 waves, 2: 128x128, 3: 64x64, 4: 256x256 with 8 waves, 5: 256x256 with 8
+ * waves on 16x16x32 matrix instructions; fp32 always uses 64x64); other
+ * values give DIT_ERR_INVALID_ARG. */
 enum { DIT_EPI_STORE = 0, DIT_EPI_GELU = 1, DIT_EPI_RESIDUAL = 2, DIT_EPI_STORE_F32 = 3 };
 dit_status dit_gemm(int32_t dtype, int32_t epilogue, const void *A, int64_t lda, const void *W,
                     int64_t ldw, int32_t M, int32_t N, int32_t K, const void *bias, void *out,

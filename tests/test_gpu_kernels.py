@@ -45,7 +45,7 @@ def _gemm_case(dtype, epi, M, N, K, tile, seed=0, with_bias=True, with_gate=True
     return rel_l2(got, ref)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
                                  B.DIT_EPI_STORE_F32])
 @pytest.mark.parametrize("M,N,K", [(1000, 700, 520), (300, 260, 64), (513, 1024, 1536)])
@@ -86,7 +86,7 @@ def test_gemm_bf16_three_stage_ring(epi, M, N, K):
     assert err < tol, err
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("epi", [B.DIT_EPI_STORE, B.DIT_EPI_GELU, B.DIT_EPI_RESIDUAL,
                                  B.DIT_EPI_STORE_F32])
 def test_gemm_bf16_without_bias_or_gate(tile, epi):
