@@ -352,15 +352,25 @@ __device__ __forceinline__ void att_exp_half(const f32x16 &x, bf16x8 &lo, bf16x8
 
 template <int HD, int NW, int KS = 1>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) void attention_bf16_kernel(AttnArgs p) {
-  // Hardware order: workgroups of consecutive query blocks go to different
-  // XCDs, so every XCD's L2 fetches the K and V^T of every head.  An order
-  // that gave each XCD a contiguous range of (query block, head) pairs cut
-  // the image_s self-attention's fetched bytes from 28.5 to 7.5 MB per launch
-  // and the launch itself got ~1 % faster, but the image_s step got 0.55 %
-  // slower (the output projection then finds less of its input in the XCD's
-  // own L2) and the Wan-14B step did not change; it was removed.
-  const int bx = blockIdx.x, by = blockIdx.y;
-  att_select_batch(p, 2, blockIdx.z);
+  // Workgroup order.  Without a key split (the long sequences) every XCD
+  // takes one contiguous range of (query block, head, sequence) triples,
+  // query blocks fastest, so its L2 fetches the K and V^T of the one or two
+  // heads in its range instead of every head's (Wan-14B self-attention: 3.4
+  // instead of 6.0 GB per launch, same time).  The key-split grids of short
+  // sequences keep the hardware order: there the contiguous order cut the
+  // image_s self-attention's bytes from 28.5 to 7.5 MB per launch, but the
+  // step got 0.55 % slower, its output projection finding less of its input
+  // in its own XCD's L2.
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if constexpr (KS == 1) {
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int wg = xcd_contiguous(blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z),
+                                  gx * gy * gridDim.z);
+    bx = wg % gx;
+    by = (wg / gx) % gy;
+    bz = wg / (gx * gy);
+  }
+  att_select_batch(p, 2, bz);
   typedef bf16x8 F;
   constexpr int KROWB = HD * 2;            // bytes per K row
   constexpr int KCHUNK = KROWB / 16;       // 16-byte chunks per K row

@@ -546,7 +546,12 @@ template <int EPI, int NWN = 4, int NW = 8>
 __global__ __launch_bounds__(64 * NW) void gemm16_kernel(GemmArgs p) {
   typedef bf16 T;
   constexpr int BM = 256, BN = 256, NT = 64 * NW;
-  constexpr int BK = 64, VEC = 8, ROW = BK + VEC, CHUNKS = BK / 32;
+  // LDS rows of 128 bytes (64 k) without padding; the 16-byte chunk c of row
+  // r is stored at chunk c ^ (r & 7).  A 16-row fragment read (lane l: row
+  // l % 16, chunk 4 ch + l / 16) then meets no bank conflicts: with rows padded
+  // to 144 bytes, as the 32x32x16 loop has them, the same reads took 1.7x as
+  // long in an LDS probe, and the kernel counted 60x the conflict cycles.
+  constexpr int BK = 64, VEC = 8, ROW = BK, CHUNKS = BK / 32;
   // 8 waves: 128 x 64 per wave as 8 x 4 accumulators.  (4 waves of 128 x 128,
   // one wave per SIMD with the accumulators in AGPRs, also fit this code; they
   // were 16-27 % slower on the step shapes.)
@@ -589,9 +594,12 @@ __global__ __launch_bounds__(64 * NW) void gemm16_kernel(GemmArgs p) {
     else
       stage[i] = buf_load16(rw_src, kin ? w_off0 + (i - LA) * w_step + kb : OOB);
   };
+  // r0 + RPP i and BM + ... share r0's low three bits (RPP and BM are
+  // multiples of 8), so the stored chunk is the same for every piece
+  const int kk_sw = (((tid & 7) ^ (r0 & 7)) * VEC);
   auto sstore_piece = [&](int i, T *base) {
     const int row = i < LA ? r0 + RPP * i : BM + r0 + RPP * (i - LA);
-    *reinterpret_cast<U128 *>(base + row * ROW + kk) = stage[i];
+    *reinterpret_cast<U128 *>(base + row * ROW + kk_sw) = stage[i];
   };
 
   f32x4 acc[TM][TN];
@@ -600,14 +608,19 @@ __global__ __launch_bounds__(64 * NW) void gemm16_kernel(GemmArgs p) {
 #pragma unroll
     for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int arow = (wm * WM + (lane & 15)) * ROW + (lane >> 4) * 8;
-  const int wrow = (BM + wn * WN + (lane & 15)) * ROW + (lane >> 4) * 8;
+  // every fragment row of this lane has low bits (lane & 7): its chunk of
+  // k-chunk ch is (4 ch + lane / 16) ^ (lane & 7)
+  const int arow = (wm * WM + (lane & 15)) * ROW;
+  const int wrow = (BM + wn * WN + (lane & 15)) * ROW;
+  int chk[CHUNKS];
+#pragma unroll
+  for (int ch = 0; ch < CHUNKS; ++ch) chk[ch] = ((ch * 4 + (lane >> 4)) ^ (lane & 7)) * VEC;
   bf16x8 ar[RING], wf[2][TN];
   auto afrag = [&](const T *base, int ch, int a) {
-    return *reinterpret_cast<const bf16x8 *>(base + arow + a * 16 * ROW + ch * 32);
+    return *reinterpret_cast<const bf16x8 *>(base + arow + a * 16 * ROW + chk[ch]);
   };
   auto wfrag = [&](const T *base, int ch, int b) {
-    return *reinterpret_cast<const bf16x8 *>(base + wrow + b * 16 * ROW + ch * 32);
+    return *reinterpret_cast<const bf16x8 *>(base + wrow + b * 16 * ROW + chk[ch]);
   };
 
   const int KT = (K + BK - 1) / BK;
