@@ -67,7 +67,10 @@ def gemm(dtype: str, epilogue: int, A, W, bias, out, gate=None, tile: int = 0, s
 class DeviceDiT:
     def __init__(self, cfg, params: dict, device: str = "cuda", stream: int | None = None,
                  guidance: bool = False, offload: bool = False, pack_offload: bool = True,
-                 cache: bool = False):
+                 cache: bool = False, workspace: torch.Tensor | None = None):
+        """`workspace`: an optional caller-owned uint8 device tensor of at least
+        dit_workspace_size bytes, 256-byte aligned, that the handle uses instead
+        of allocating its own; its contents on entry do not matter."""
         self.cfg = cfg
         self.device = torch.device(device)
         self.c = B.make_config(cfg, guidance, offload, cache)
@@ -122,7 +125,14 @@ class DeviceDiT:
         self._w.global_ = gw
         self._w.blocks = ctypes.cast(self._blocks, ctypes.POINTER(B.dit_block_weights))
         self.ws_bytes = B.dit_workspace_size(self.c)
-        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        if workspace is None:
+            workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
+        elif (workspace.dtype != torch.uint8 or workspace.device.type != self.device.type
+              or (self.device.index is not None and workspace.device.index != self.device.index)
+              or not workspace.is_contiguous() or workspace.numel() < self.ws_bytes):
+            raise ValueError(f"workspace must be a contiguous uint8 tensor of at least "
+                             f"{self.ws_bytes} bytes on {self.device}")
+        self.workspace = workspace
         self.handle = B.dit_create(self.c, self._w, self.workspace.data_ptr(), self.ws_bytes,
                                    self._stream(stream))
 

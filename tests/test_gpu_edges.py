@@ -103,3 +103,64 @@ def test_guided_step_one_token_contexts():
     tol = tolerances(cfg)
     assert rel_l2(to_np(v), Vo) < tol["velocity"]
     assert rel_l2(to_np(X), Xo) < tol["latents"]
+
+
+def _poisoned(m_bytes):
+    # every byte 0xFF: a NaN in float32 and in bfloat16 alike
+    return torch.full((m_bytes,), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("name,over", [("tiny_f32", dict(num_blocks=3)),
+                                       ("image_s_bf16", dict(latent=(1, 10, 16), num_blocks=3))])
+def test_poisoned_workspace_plain_guided_and_cached(name, over):
+    # a workspace that starts as NaN everywhere gives bitwise the result of a
+    # fresh one, at token counts that are not a multiple of the 64-row tiles
+    # (16 and 40; guidance needs a multiple of 8) and a 5-token context:
+    # no kernel reads workspace memory (padding rows, key/value tails, cache
+    # factors) that the step has not written first
+    require_gpu()
+    cfg = workload(name, **over)
+    announce("poisoned workspace", name, cfg.tokens)
+    prm = SP.make_params(cfg)
+    X0 = SP.make_latents(cfg)
+    E, En = SP.make_ctx(cfg, length=5), SP.make_ctx(cfg, seed=3, length=5)
+    Ed, End = dev_tensor(E, cfg.dtype), dev_tensor(En, cfg.dtype)
+    sig = oracle.flow_sigmas(cfg.steps, cfg.shift)
+    sched = [(float(np.float32(1000.0 * sig[i])), float(np.float32(sig[i])),
+              float(np.float32(sig[i + 1]))) for i in range(min(cfg.steps, 6))]
+
+    def run(m, kind):
+        X = torch.from_numpy(X0).cuda()
+        v = torch.empty_like(X)
+        vs = []
+        if kind == "cached":
+            m.cache_begin(fn=1, bn=1, warmup=2, rdt=float("inf"), max_consecutive=2,
+                          taylorseer=True, ts_order=1)
+        for t, s0, s1 in (sched if kind == "cached" else sched[:1]):
+            if kind == "plain":
+                m.denoise_step(X, Ed, t, s0, s1, v_out=v)
+            elif kind == "guided":
+                m.denoise_step_cfg(X, Ed, End, t, s0, s1, 4.0, v_out=v)
+            else:
+                m.denoise_step_cached(X, Ed, t, s0, s1, ctx_neg=End, guidance_scale=4.0, v_out=v)
+            torch.cuda.synchronize()
+            vs.append(to_np(v))
+        return to_np(X), vs
+
+    for kind, kw in [("plain", {}), ("guided", dict(guidance=True)),
+                     ("cached", dict(guidance=True, cache=True))]:
+        ref = DeviceDiT(cfg, prm, **kw)
+        Xr, vr = run(ref, kind)
+        ws = _poisoned(ref.ws_bytes)
+        ref.close()
+        m = DeviceDiT(cfg, prm, workspace=ws, **kw)
+        Xp, vp = run(m, kind)
+        m.close()
+        assert np.isfinite(Xp).all(), kind
+        assert np.array_equal(Xp, Xr), kind
+        assert all(np.array_equal(a, b) for a, b in zip(vp, vr)), kind
+    # and the plain step itself against the oracle
+    t, s0, s1 = sched[0]
+    Vo = oracle.dit_forward(X0, E, t, prm, cfg)
+    m = DeviceDiT(cfg, prm, workspace=_poisoned(ref.ws_bytes))
+    assert rel_l2(run(m, "plain")[1][0], Vo) < tolerances(cfg)["velocity"]
