@@ -131,7 +131,7 @@ def _attention_case(cfg, sq, sk, v_const=None, rng=RNG):
     # small grids split the keys in two ranges: even tile counts, ragged last tile
     ("image_s_bf16", 200, 250), ("image_s_bf16", 100, 2000),
     ("wan1p3b_bf16", 777, 1500), ("wan1p3b_bf16", 256, 512), ("wan1p3b_bf16", 64, 3),
-    # >= 256 workgroups of 256 queries: the two-query-block kernel (head_dim 128)
+    # head_dim 128 at 40 and 28 heads, key counts under the eight-wave threshold
     ("wan14b_bf16", 1700, 1000), ("wan14b_bf16", 1537, 64), ("image_l_bf16", 2400, 777),
 ])
 def test_attention_parity(name, sq, sk):
@@ -155,6 +155,50 @@ def test_attention_constant_values(name, sk):
     announce("attention V=1", name, sk)
     o, *_ = _attention_case(cfg, 200, sk, v_const=1.0)
     assert np.max(np.abs(o - 1.0)) <= 2 ** -7
+
+
+@pytest.mark.parametrize("name,sq,sk", [
+    ("image_s_bf16", 200, 2000),     # head_dim 64, two key ranges
+    ("image_s_bf16", 2600, 4100),    # head_dim 64, eight waves, one key range
+    ("wan1p3b_bf16", 777, 1500),     # head_dim 128, two key ranges
+    ("image_l_bf16", 600, 4150),     # head_dim 128, two key ranges
+    ("wan14b_bf16", 800, 4100),      # head_dim 128, eight waves, one key range
+])
+def test_attention_running_max_moves(name, sq, sk):
+    # Scores that rise along the keys: a ramp of 40 (natural-log units) on
+    # the first channel of every head, so a later key's score exceeds the
+    # first tile's maximum by far more than 2^16 in p.  The running maximum
+    # then has to move several times, in every key range, with the largest
+    # scores in the ragged last tile (its masked keys included).
+    require_gpu()
+    cfg = workload(name)
+    H, d, D = cfg.heads, cfg.head_dim, cfg.hidden
+    announce("attention running max", name, sq, sk)
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((sq, H, d)) * 0.5
+    k = rng.standard_normal((sk, H, d)) * 0.5
+    a = 8.0
+    q[:, :, 0] += a
+    k[:, :, 0] += (40.0 * np.sqrt(d) / a) * np.arange(sk)[:, None] / sk
+    q = storage_round(q.reshape(sq, D), cfg.dtype)
+    k = storage_round(k.reshape(sk, D), cfg.dtype)
+    v = storage_round(rng.standard_normal((sk, D)), cfg.dtype)
+    # the inputs do take the rare path: in log2 units, for every query and
+    # head, some key beats the first 64 keys' maximum by more than 16
+    lg = np.einsum("qhd,khd->qhk", q.reshape(sq, H, d)[:64], k.reshape(sk, H, d)) \
+        / np.sqrt(d) / np.log(2.0)
+    assert np.all(lg.max(-1) - lg[:, :, :64].max(-1) > 16.0)
+    ldv = (sk + 63) // 64 * 64
+    vt = np.zeros((D, ldv))
+    vt[:, :sk] = v.T
+    qd, kd, vtd = dev_tensor(q, cfg.dtype), dev_tensor(k, cfg.dtype), dev_tensor(vt, cfg.dtype)
+    od = torch.empty_like(qd)
+    attention(cfg.dtype, H, d, qd, kd, vtd, od, sq, sk)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q.reshape(sq, H, d), k.reshape(sk, H, d), v.reshape(sk, H, d))
+    err = rel_l2(to_np(od), ref.reshape(sq, -1))
+    print(f"[attention running max] {name} {sq}x{sk}: {err:.2e}", flush=True)
+    assert np.isfinite(to_np(od)).all() and err < 1e-2
 
 
 # ----------------------------------------------------------------- one block, teacher-forced
