@@ -108,14 +108,14 @@ def test_layernorm_modulate_widths(D):
 
 
 # ----------------------------------------------------------------- attention
-def _attention_case(cfg, sq, sk, v_const=None, rng=RNG):
+def _attention_case(cfg, sq, sk, v_const=None, rng=RNG, pad=0.0):
     H, d, D = cfg.heads, cfg.head_dim, cfg.hidden
     q = storage_round(rng.standard_normal((sq, D)), cfg.dtype)
     k = storage_round(rng.standard_normal((sk, D)), cfg.dtype)
     v = storage_round(rng.standard_normal((sk, D)), cfg.dtype) if v_const is None \
         else np.full((sk, D), v_const)
     ldv = (sk + 63) // 64 * 64
-    vt = np.zeros((D, ldv))
+    vt = np.full((D, ldv), pad)
     vt[:, :sk] = v.T
     qd, kd, vtd = dev_tensor(q, cfg.dtype), dev_tensor(k, cfg.dtype), dev_tensor(vt, cfg.dtype)
     od = torch.empty_like(qd)
@@ -143,6 +143,24 @@ def test_attention_parity(name, sq, sk):
     ref = oracle.attention(q.reshape(sq, H, d), k.reshape(sk, H, d), v.reshape(sk, H, d))
     tol = 1e-5 if cfg.dtype == "f32" else 1e-2
     assert rel_l2(o, ref.reshape(sq, -1)) < tol
+
+
+@pytest.mark.parametrize("name,sq,sk", [
+    ("tiny_f32", 130, 77), ("image_s_bf16", 300, 1000), ("image_s_bf16", 200, 250),
+    ("image_s_bf16", 2600, 4100), ("wan1p3b_bf16", 777, 1500), ("wan14b_bf16", 800, 4100),
+])
+def test_attention_nan_value_padding(name, sq, sk):
+    # the caller's V^T columns past the last key (up to the 64-key padded
+    # stride) hold NaN: the kernels clear them in the ragged last tile instead
+    # of multiplying them by a zero P, so the result is the oracle's
+    require_gpu()
+    cfg = workload(name)
+    announce("attention NaN padding", name, sq, sk)
+    o, q, k, v = _attention_case(cfg, sq, sk, pad=np.nan)
+    H, d = cfg.heads, cfg.head_dim
+    ref = oracle.attention(q.reshape(sq, H, d), k.reshape(sk, H, d), v.reshape(sk, H, d))
+    tol = 1e-5 if cfg.dtype == "f32" else 1e-2
+    assert np.isfinite(o).all() and rel_l2(o, ref.reshape(sq, -1)) < tol
 
 
 @pytest.mark.parametrize("name,sk", [("image_s_bf16", 333), ("image_s_bf16", 1000),
