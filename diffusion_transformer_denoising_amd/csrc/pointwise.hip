@@ -26,16 +26,21 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x
   if (row >= rows) return;
   const float *xr = x + (int64_t)row * D;
   const int nv = D >> 2;  // float4 count
-  f32x4 v[NV], sh[NV], sc[NV];
-  // the modulation vectors go out with the row: read after the reductions,
-  // each group's load would be another memory round trip before its store
-  if (shift) {
+  // Narrow rows: the modulation vectors go out with the row (read after the
+  // reductions, each group's load would be another memory round trip before
+  // its store).  Wide rows (more than 8 float4 per lane) read them in the
+  // store loop instead: held from the start they would take 8 NV more
+  // registers and leave two waves per SIMD at width 5120, too few rows in
+  // flight to cover the memory latency.
+  constexpr bool EARLY = NV <= 8;
+  f32x4 v[NV], sh[EARLY ? NV : 1], sc[EARLY ? NV : 1];
+  if (EARLY && shift) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = lane + i * 64;
       if (c < nv) {
-        sh[i] = *reinterpret_cast<const f32x4 *>(shift + 4 * c);
-        sc[i] = *reinterpret_cast<const f32x4 *>(scale + 4 * c);
+        sh[EARLY ? i : 0] = *reinterpret_cast<const f32x4 *>(shift + 4 * c);
+        sc[EARLY ? i : 0] = *reinterpret_cast<const f32x4 *>(scale + 4 * c);
       }
     }
   }
@@ -70,8 +75,16 @@ __global__ __launch_bounds__(256) void ln_mod_kernel(const float *__restrict__ x
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = (v[i][e] - mu) * rstd;
       if (shift) {
+        f32x4 shv, scv;
+        if constexpr (EARLY) {
+          shv = sh[EARLY ? i : 0];
+          scv = sc[EARLY ? i : 0];
+        } else {
+          shv = *reinterpret_cast<const f32x4 *>(shift + 4 * c);
+          scv = *reinterpret_cast<const f32x4 *>(scale + 4 * c);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = o[e] * (1.0f + sc[i][e]) + sh[i][e];
+        for (int e = 0; e < 4; ++e) o[e] = o[e] * (1.0f + scv[e]) + shv[e];
       }
       if constexpr (sizeof(T) == 2) {
         bf16x4 b;
