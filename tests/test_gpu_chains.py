@@ -1,15 +1,18 @@
-"""Chains at the full video shape and the cached guided run at the pages' knob.
+"""Chains at the full video and large-image shapes, and the cached guided run
+at the pages' knob.
 
-* Full-depth Wan-1.3B model (30 blocks, every block with its own weights):
-  the residual stream is carried through all 30 blocks on the GPU, and blocks
-  0, 15 and 29 are checked teacher-forced (the oracle takes the GPU's input of
-  that block) on sampled rows; the denoise step of the same model is checked
-  on sampled tokens against the head applied to the GPU's last block output.
-* A truncated chain at the real Wan-1.3B sizes: two blocks, two denoise steps
-  of the shifted schedule.  Every block of every step is checked
-  teacher-forced on sampled rows, every step's velocity on sampled tokens, and
-  the latents after both steps against the oracle's two Euler updates
-  accumulated on the same tokens.  (An untruncated float64 chain over all
+* Full-depth Wan-1.3B and 6B-image models (30 blocks each, every block with
+  its own weights): the residual stream is carried through all 30 blocks on
+  the GPU, and blocks 0, 15 and 29 are checked teacher-forced (the oracle
+  takes the GPU's input of that block) on sampled rows; the denoise step of
+  the same model is checked on sampled tokens against the head applied to
+  the GPU's last block output.  (The oracle's own 30-block float64 step at
+  the 6B-image shape, 55 TFLOP, would take minutes of host time.)
+* Truncated chains at the real Wan-1.3B, 6B-image and Wan-14B sizes: two
+  blocks, two denoise steps of each workload's schedule.  Every block of
+  every step is checked teacher-forced on sampled rows, every step's velocity
+  on sampled tokens, and the latents after both steps against the oracle's
+  two Euler updates accumulated on the same tokens.  (An untruncated float64 chain over all
   32760 tokens needs the full 32760 x 32760 attention per head and block, far
   beyond the test's time; the sampled outputs see every token through K and
   V.)
@@ -61,10 +64,11 @@ def _check_block(got_rows, x_in, c, mod, p, cfg, pos, rows, what):
     return ref
 
 
-def test_full_depth_blocks_and_step_wan1p3b():
+@pytest.mark.parametrize("name", ["wan1p3b_bf16", "image_l_bf16"])
+def test_full_depth_blocks_and_step(name):
     require_gpu()
-    cfg = workload("wan1p3b_bf16")
-    announce("full depth wan1p3b", cfg.num_blocks, "blocks")
+    cfg = workload(name)
+    announce("full depth", name, cfg.num_blocks, "blocks")
     prm = SP.make_params(cfg)
     g = prm["global"]
     m = DeviceDiT(cfg, prm)
@@ -85,7 +89,7 @@ def test_full_depth_blocks_and_step_wan1p3b():
         torch.cuda.synchronize()
         if b in check:
             _check_block(to_np(x)[rows], x_in, c, mod, prm["blocks"][b], cfg, pos, rows,
-                         f"wan1p3b block {b} of {cfg.num_blocks}")
+                         f"{name} block {b} of {cfg.num_blocks}")
     # the step of the same model: its velocity at the sampled tokens against
     # the head on the GPU's own last block output
     u = oracle.final_layer(to_np(x)[rows], temb, g, cfg)
@@ -96,14 +100,15 @@ def test_full_depth_blocks_and_step_wan1p3b():
     ev = rel_l2(oracle.patchify(to_np(v), cfg.patch)[rows], u)
     ref = oracle.euler_step(oracle.patchify(X0, cfg.patch)[rows], u, s0, s1)
     ex = rel_l2(oracle.patchify(to_np(Xd), cfg.patch)[rows], ref)
-    print(f"[chain] wan1p3b 30-block step: velocity {ev:.2e} latents {ex:.2e}", flush=True)
+    print(f"[chain] {name} {cfg.num_blocks}-block step: velocity {ev:.2e} latents {ex:.2e}", flush=True)
     assert ev < tolerances(cfg)["velocity"] and ex < tolerances(cfg)["latents"]
 
 
-def test_truncated_chain_two_blocks_two_steps_wan1p3b():
+@pytest.mark.parametrize("name", ["wan1p3b_bf16", "image_l_bf16", "wan14b_bf16"])
+def test_truncated_chain_two_blocks_two_steps(name):
     require_gpu()
-    cfg = workload("wan1p3b_bf16", num_blocks=2)
-    announce("truncated chain wan1p3b 2 blocks x 2 steps")
+    cfg = workload(name, num_blocks=2)
+    announce("truncated chain", name, "2 blocks x 2 steps")
     prm = SP.make_params(cfg)
     g = prm["global"]
     m = DeviceDiT(cfg, prm)
@@ -128,14 +133,14 @@ def test_truncated_chain_two_blocks_two_steps_wan1p3b():
             m.block_forward(b, x, cd, torch.from_numpy(mod).cuda())
             torch.cuda.synchronize()
             ref = _check_block(to_np(x)[rows], x_in, c, mod, prm["blocks"][b], cfg, pos, rows,
-                               f"step {k} block {b}")
+                               f"{name} step {k} block {b}")
         u = oracle.final_layer(ref, temb, g, cfg)
         m.denoise_step(X, Ed, t, s0, s1, v_out=v)
         torch.cuda.synchronize()
         ev = rel_l2(oracle.patchify(to_np(v), cfg.patch)[rows], u)
         X_acc = oracle.euler_step(X_acc, u, s0, s1)
         ex = rel_l2(oracle.patchify(to_np(X), cfg.patch)[rows], X_acc)
-        print(f"[chain] step {k}: velocity {ev:.2e} latents {ex:.2e}", flush=True)
+        print(f"[chain] {name} step {k}: velocity {ev:.2e} latents {ex:.2e}", flush=True)
         assert ev < tol["velocity"] and ex < tol["latents"], (k, ev, ex)
 
 
