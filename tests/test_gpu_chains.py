@@ -1,13 +1,19 @@
 """Chains at the full video and large-image shapes, and the cached guided run
 at the pages' knob.
 
-* Full-depth Wan-1.3B and 6B-image models (30 blocks each, every block with
-  its own weights): the residual stream is carried through all 30 blocks on
-  the GPU, and blocks 0, 15 and 29 are checked teacher-forced (the oracle
-  takes the GPU's input of that block) on sampled rows; the denoise step of
+* Full-depth Wan-1.3B, 6B-image and Wan-14B models (30, 30 and 40 blocks,
+  every block with its own weights): the residual stream is carried through
+  every block on the GPU, and blocks 0, B/2 and B-1 are checked teacher-forced
+  (the oracle takes the GPU's input of that block) on sampled rows; the
+  denoise step of
   the same model is checked on sampled tokens against the head applied to
   the GPU's last block output.  (The oracle's own 30-block float64 step at
-  the 6B-image shape, 55 TFLOP, would take minutes of host time.)
+  the 6B-image shape, 55 TFLOP, would take minutes of host time.)  At the
+  Wan-14B shape, rounding differences grow through the 40 random-init blocks:
+  two bf16 evaluations of the same chain whose modulation differs by 3e-7
+  end about 0.1 apart (at Wan-1.3B, 4e-3).  The test measures that spread
+  and holds the step's velocity to the bar or to twice the spread; the
+  blocks and the latents keep their bars.
 * Truncated chains at the real Wan-1.3B, 6B-image and Wan-14B sizes: two
   blocks, two denoise steps of each workload's schedule.  Every block of
   every step is checked teacher-forced on sampled rows, every step's velocity
@@ -64,7 +70,7 @@ def _check_block(got_rows, x_in, c, mod, p, cfg, pos, rows, what):
     return ref
 
 
-@pytest.mark.parametrize("name", ["wan1p3b_bf16", "image_l_bf16"])
+@pytest.mark.parametrize("name", ["wan1p3b_bf16", "image_l_bf16", "wan14b_bf16"])
 def test_full_depth_blocks_and_step(name):
     require_gpu()
     cfg = workload(name)
@@ -72,6 +78,13 @@ def test_full_depth_blocks_and_step(name):
     prm = SP.make_params(cfg)
     g = prm["global"]
     m = DeviceDiT(cfg, prm)
+    check = {0, cfg.num_blocks // 2, cfg.num_blocks - 1}
+    # the host copies of the other blocks are no longer needed (the Wan-14B
+    # weights are 57 GB in float32)
+    tables = [p["table"] for p in prm["blocks"]]
+    for b in range(cfg.num_blocks):
+        if b not in check:
+            prm["blocks"][b] = None
     X0 = SP.make_latents(cfg)
     E = SP.make_ctx(cfg)
     t, s0, s1 = _sched(cfg, 8)[7]
@@ -81,9 +94,8 @@ def test_full_depth_blocks_and_step(name):
     pos = oracle.token_positions(cfg.grid)
     rows = _rows(cfg.tokens, 24, 41)
     x = torch.from_numpy(_embedded(X0, cfg, g)).cuda()
-    check = {0, cfg.num_blocks // 2, cfg.num_blocks - 1}
     for b in range(cfg.num_blocks):
-        mod = oracle.block_modulation(e, prm["blocks"][b]["table"]).astype(np.float32)
+        mod = oracle.block_modulation(e, tables[b]).astype(np.float32)
         x_in = to_np(x) if b in check else None
         m.block_forward(b, x, cd, torch.from_numpy(mod).cuda())
         torch.cuda.synchronize()
@@ -92,7 +104,8 @@ def test_full_depth_blocks_and_step(name):
                          f"{name} block {b} of {cfg.num_blocks}")
     # the step of the same model: its velocity at the sampled tokens against
     # the head on the GPU's own last block output
-    u = oracle.final_layer(to_np(x)[rows], temb, g, cfg)
+    xg = to_np(x)
+    u = oracle.final_layer(xg[rows], temb, g, cfg)
     Xd = torch.from_numpy(X0).cuda()
     v = torch.empty_like(Xd)
     m.denoise_step(Xd, dev_tensor(E, cfg.dtype), t, s0, s1, v_out=v)
@@ -100,8 +113,24 @@ def test_full_depth_blocks_and_step(name):
     ev = rel_l2(oracle.patchify(to_np(v), cfg.patch)[rows], u)
     ref = oracle.euler_step(oracle.patchify(X0, cfg.patch)[rows], u, s0, s1)
     ex = rel_l2(oracle.patchify(to_np(Xd), cfg.patch)[rows], ref)
-    print(f"[chain] {name} {cfg.num_blocks}-block step: velocity {ev:.2e} latents {ex:.2e}", flush=True)
-    assert ev < tolerances(cfg)["velocity"] and ex < tolerances(cfg)["latents"]
+    # the spread of two bf16 evaluations of the same chain: the same blocks
+    # again, with the modulation of the GPU's own time path (within 3e-7 of
+    # the oracle's); the step takes its time path, context projection and
+    # patch embedding from the GPU, so it differs from the chain above by
+    # perturbations of that size
+    bmod, _, _ = m.time_embedding(t)
+    x2 = torch.from_numpy(_embedded(X0, cfg, g)).cuda()
+    for b in range(cfg.num_blocks):
+        m.block_forward(b, x2, cd, bmod[b].contiguous())
+    torch.cuda.synchronize()
+    spread = rel_l2(oracle.final_layer(to_np(x2)[rows], temb, g, cfg), u)
+    print(f"[chain] {name} {cfg.num_blocks}-block step: velocity {ev:.2e} latents {ex:.2e} "
+          f"(two evaluations of the chain: {spread:.2e})", flush=True)
+    tol = tolerances(cfg)
+    assert ex < tol["latents"]
+    # the velocity bar, or twice the spread where bf16 rounding grows past it
+    # through the depth (the Wan-14B shape: about 0.1 after 40 blocks)
+    assert ev < max(tol["velocity"], 2.0 * spread), (ev, spread)
 
 
 @pytest.mark.parametrize("name", ["wan1p3b_bf16", "image_l_bf16", "wan14b_bf16"])
