@@ -264,11 +264,11 @@ struct Profiler {
 }  // namespace
 
 struct dit_model {
-  dit_config cfg;
-  DType dt;
-  dit_global_weights g;
+  dit_config cfg{};
+  DType dt = DT_F32;
+  dit_global_weights g{};                 // unused by block calls made without a handle
   std::vector<dit_block_weights> blocks;  // device pointers, or host ones with offload
-  char *ws;
+  char *ws = nullptr;
   Plan plan;
   Profiler prof;
   // layerwise offload: block copies run on their own stream; ready[s] marks
