@@ -19,8 +19,9 @@
  *  - Every pointer argument named as device memory must be a device address
  *    valid on the current HIP device; host arguments are plain host memory.
  *  - Device buffers are owned by the caller.  The library allocates no device
- *    memory; a model handle keeps non-owning pointers to the weights and the
- *    workspace, which must outlive it.
+ *    memory (its one device array is the static scratch of
+ *    dit_block_forward_static); a model handle keeps non-owning pointers to
+ *    the weights and the workspace, which must outlive it.
  *  - Calls that take a stream enqueue their work asynchronously on it
  *    (NULL = the default stream) and return without synchronising.
  *  - Arguments are validated before anything is enqueued: a call that returns
