@@ -23,7 +23,9 @@
  *    dit_block_forward_static); a model handle keeps non-owning pointers to
  *    the weights and the workspace, which must outlive it.
  *  - Calls that take a stream enqueue their work asynchronously on it
- *    (NULL = the default stream) and return without synchronising.
+ *    (NULL = the default stream) and return without synchronising; the one
+ *    exception is dit_denoise_step_cached on a step that may reuse the cache
+ *    (it waits for its probe, see there).
  *  - Arguments are validated before anything is enqueued: a call that returns
  *    an error has not touched any caller buffer.  Launch failures are reported
  *    as DIT_ERR_HIP.  There is no silent fallback: an unsupported shape is an
